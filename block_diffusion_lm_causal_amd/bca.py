@@ -1,0 +1,245 @@
+"""Python binding of libbca.so (ctypes): argument marshalling only.
+
+Every step of the attention runs in the library's HIP kernels; this module
+checks tensor placement, allocates outputs with torch (device memory and
+streams are all torch provides here) and passes raw pointers and sizes to the
+C ABI declared in include/bca.h.  There is no fallback: if the library is
+missing or a call fails, a ``BcaError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbca.so")
+
+BCA_F32 = 0
+BCA_BF16 = 1
+
+# Every symbol include/bca.h declares.
+EXPORTS = (
+    "bca_abi_version", "bca_status_string", "bca_last_error", "bca_fwd", "bca_staircase_fwd",
+    "bca_staircase_bwd_workspace", "bca_staircase_bwd", "bca_decode_workspace", "bca_decode",
+)
+
+
+class BcaError(RuntimeError):
+    """A libbca call returned a non-zero status, or the library is unavailable."""
+
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func}: status {status}: {message}")
+        self.func = func
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbca.so once (raises BcaError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise BcaError("load", -1, f"{LIB_PATH} is missing; build it with "
+                       "`python -m block_diffusion_lm_causal_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.bca_abi_version.restype = _I
+    L.bca_abi_version.argtypes = []
+    L.bca_status_string.restype = ctypes.c_char_p
+    L.bca_status_string.argtypes = [_I]
+    L.bca_last_error.restype = ctypes.c_char_p
+    L.bca_last_error.argtypes = []
+    L.bca_fwd.restype = _I
+    L.bca_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]
+    L.bca_staircase_fwd.restype = _I
+    L.bca_staircase_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                    _I, _P]
+    L.bca_staircase_bwd_workspace.restype = _S
+    L.bca_staircase_bwd_workspace.argtypes = [_I, _I, _I, _I]
+    L.bca_staircase_bwd.restype = _I
+    L.bca_staircase_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                    _I, _I, _I, _F, _I, _P, _S, _P]
+    L.bca_decode_workspace.restype = _S
+    L.bca_decode_workspace.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.bca_decode.restype = _I
+    L.bca_decode.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(lib().bca_abi_version())
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.bca_last_error().decode() or L.bca_status_string(status).decode()
+        raise BcaError(func, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BCA_BF16
+    if t.dtype == torch.float32:
+        return BCA_F32
+    raise BcaError("dtype", 3, f"unsupported tensor dtype {t.dtype}")
+
+
+def _need_gpu(*ts: Optional[torch.Tensor]) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise BcaError("args", 2, "tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise BcaError("args", 2, "tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise BcaError("args", 2, "tensors must share one device")
+    return dev
+
+
+def _seq_args(cu_seqlens: torch.Tensor, max_seqlen: Optional[int]):
+    if cu_seqlens.dtype != torch.int32:
+        raise BcaError("args", 2, "cu_seqlens must be int32")
+    nseq = cu_seqlens.numel() - 1
+    if max_seqlen is None:  # convenience: one device-to-host read
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+    return nseq, int(max_seqlen)
+
+
+def staircase_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                  s_copies: Optional[torch.Tensor], block_size: int,
+                  scale: Optional[float] = None, max_seqlen: Optional[int] = None,
+                  out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Staircase (or, with s_copies=None, block-causal) forward -> (O, LSE).
+
+    q [total, hq, d], k/v [total, hkv, d] (bf16 or float32), cu_seqlens int32
+    [nseq + 1] and s_copies int32 [nseq] on the same GPU.  LSE is [hq, total]
+    float32 (natural log).
+    """
+    dev = _need_gpu(q, k, v, cu_seqlens, s_copies, out, lse)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (total, hkv, d) or v.shape != k.shape:
+        raise BcaError("staircase_fwd", 2, "k and v must be [total, hkv, d] matching q")
+    nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    if s_copies is not None and (s_copies.dtype != torch.int32 or s_copies.numel() != nseq):
+        raise BcaError("staircase_fwd", 2, "s_copies must be int32 [nseq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
+    st = lib().bca_staircase_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(cu_seqlens), _ptr(s_copies), nseq, max_seqlen, total, hq,
+                                 hkv, d, int(block_size), scale, _dtype_code(q), _stream(dev))
+    _check("bca_staircase_fwd", st)
+    return out, lse
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+        block_size: int, scale: Optional[float] = None, max_seqlen: Optional[int] = None,
+        out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-causal forward over packed sequences -> (O, LSE); see staircase_fwd."""
+    dev = _need_gpu(q, k, v, cu_seqlens, out, lse)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (total, hkv, d) or v.shape != k.shape:
+        raise BcaError("fwd", 2, "k and v must be [total, hkv, d] matching q")
+    nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
+    st = lib().bca_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), nseq,
+                       max_seqlen, total, hq, hkv, d, int(block_size), scale, _dtype_code(q),
+                       _stream(dev))
+    _check("bca_fwd", st)
+    return out, lse
+
+
+def staircase_bwd_workspace(total: int, hq: int, hkv: int, d: int) -> int:
+    return int(lib().bca_staircase_bwd_workspace(total, hq, hkv, d))
+
+
+def staircase_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                  lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor,
+                  s_copies: Optional[torch.Tensor], block_size: int,
+                  scale: Optional[float] = None, max_seqlen: Optional[int] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None):
+    """Backward -> (dQ, dK, dV), bf16.  o and lse come from staircase_fwd."""
+    dev = _need_gpu(q, k, v, o, lse, dout, cu_seqlens, s_copies, workspace, dq, dk, dv)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = staircase_bwd_workspace(total, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().bca_staircase_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), _ptr(s_copies),
+                                 nseq, max_seqlen, total, hq, hkv, d, int(block_size), scale,
+                                 _dtype_code(q), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("bca_staircase_bwd", st)
+    return dq, dk, dv
+
+
+def decode_workspace(q_len: int, kv_len: int, hq: int, hkv: int, d: int,
+                     num_splits: int = 0) -> int:
+    return int(lib().bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+           num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode step -> (O [q_len, hq, d], LSE [hq, q_len]); k/v hold prefix + block rows."""
+    dev = _need_gpu(q, k, v, workspace, out, lse)
+    q_len, hq, d = q.shape
+    kv_len, hkv = k.shape[0], k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
+    st = lib().bca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv,
+                          d, scale, _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
+                          _stream(dev))
+    _check("bca_decode", st)
+    return out, lse

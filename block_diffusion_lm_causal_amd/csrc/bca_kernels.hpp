@@ -1,0 +1,83 @@
+// Kernel argument blocks and host launchers of the bca library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bca {
+
+// Forward over packed segments (block-causal when s_copies is NULL).
+struct FwdArgs {
+  const uint16_t* q;  // [total, hq, d] bf16
+  const uint16_t* k;  // [total, hkv, d]
+  const uint16_t* v;
+  uint16_t* o;        // [total, hq, d]
+  float* lse;         // [hq, total]
+  const int32_t* cu_seqlens;
+  const int32_t* s_copies;  // may be NULL
+  int nseq, total, hq, hkv, d, block_size;
+  int hpw;            // query heads per workgroup (4, 2 or 1; divides hq / hkv)
+  float scale_log2;   // scale * log2(e)
+};
+
+struct FwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const int32_t* cu_seqlens;
+  const int32_t* s_copies;
+  int nseq, total, hq, hkv, d, block_size;
+  float scale_log2;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;  // [q_len, hq, d]
+  const uint16_t* k;  // [kv_len, hkv, d]
+  const uint16_t* v;
+  uint16_t* o;        // [q_len, hq, d]
+  float* lse;         // [hq, q_len]
+  float* part_o;      // [nsplit, q_len, hq, d] (nsplit > 1)
+  float* part_lse;    // [nsplit, hq, q_len]
+  int q_len, kv_len, hq, hkv, d, hpw;
+  int chunk;          // keys per split (multiple of 64)
+  int nsplit;
+  float scale_log2;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;      // [total, hq, d] float32 workspace
+  float* delta;       // [hq, total] float32 workspace
+  const int32_t* cu_seqlens;
+  const int32_t* s_copies;
+  int nseq, total, hq, hkv, d, block_size;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+};
+
+// Query rows of one wave are 32 consecutive tokens of one head; a workgroup
+// of four waves covers hpw heads of one KV group.
+inline int heads_per_wg(int hq, int hkv) {
+  const int group = hq / hkv;
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int ntiles_max, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdF32Args& a, int max_seqlen, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream);
+
+}  // namespace bca

@@ -1,0 +1,173 @@
+/*
+ * bca.h -- block-causal / staircase attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbca.so.  Plain pointers and sizes only; no HIP, torch or C++
+ * types appear in the signatures.  A `stream` argument is a hipStream_t passed
+ * as void* (NULL = the default stream).
+ *
+ * The attention computed is the one of "On-Policy Residual Learning for
+ * Diffusion Language Models":
+ *   - block-causal attention (thread page, highlight 3): with block size B,
+ *     query i of a sequence attends to key j iff floor(j/B) <= floor(i/B),
+ *     i.e. bidirectionally inside its own block and to every earlier block;
+ *   - staircase packed replay (paper cards page, Figure 3 caption; thread page,
+ *     Insight 3): a trajectory is a clean prefix of P tokens followed by S
+ *     copies of one B-token block.  Prefix queries are block-causal inside the
+ *     prefix; a query of copy c attends to the whole prefix and to copy c only;
+ *   - the decode step (thread page, Result 4: each block's denoising loop):
+ *     the B queries of the current block attend, unmasked, to a prefix KV cache
+ *     followed by the block's own B keys/values.
+ * O = softmax(scale * Q K^T restricted to admitted keys) V, and
+ * LSE = ln(sum over admitted keys of exp(scale * q.k)) per query row.
+ *
+ * Layouts (all row-major, contiguous, every pointer 16-byte aligned):
+ *   q, o, dout, dq : [total, hq,  d]
+ *   k, v, dk, dv   : [total, hkv, d]
+ *   lse            : [hq, total] float32
+ *   cu_seqlens     : int32 [nseq + 1] on the device, cu_seqlens[0] = 0,
+ *                    non-decreasing, cu_seqlens[nseq] = total; segment s holds
+ *                    tokens [cu_seqlens[s], cu_seqlens[s+1]).  Segments never
+ *                    attend to each other and block indices restart at the
+ *                    start of every segment.
+ *   s_copies       : int32 [nseq] on the device (S per segment) or NULL (all 0).
+ *                    With S > 0 a segment of L tokens must satisfy
+ *                    L - S*B >= 0 and (L - S*B) % B == 0.
+ * GQA head map: query head h reads KV head h / (hq / hkv); hq % hkv == 0.
+ * Element type: BCA_BF16 (bfloat16 inputs and outputs, float32 accumulation)
+ * or BCA_F32 (float32 throughout; forward only).  LSE is always float32.
+ *
+ * Ownership: the caller allocates and frees every buffer, workspaces
+ * included.  The library never allocates, frees or synchronises: each call
+ * only enqueues kernels on `stream` and returns.  Inputs are read-only and
+ * outputs must not alias inputs.  Device-array contents (cu_seqlens,
+ * s_copies) are the caller's contract and are not checked.
+ *
+ * Errors: every host-detectable fault (NULL pointer, bad shape or size,
+ * unsupported head_dim or dtype, workspace too small) is reported by the
+ * return value before anything is enqueued.  A failed kernel launch returns
+ * BCA_ERR_HIP.  bca_last_error() gives a message for the calling thread's most
+ * recent failure.  Faults inside kernels surface at the caller's next
+ * synchronisation, as with any asynchronous GPU work.
+ */
+#ifndef BCA_H
+#define BCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BCA_ABI_VERSION 1
+
+typedef enum {
+  BCA_OK = 0,
+  BCA_ERR_NULL = 1,        /* a required pointer is NULL */
+  BCA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  BCA_ERR_DTYPE = 3,       /* element type not supported by this entry point */
+  BCA_ERR_UNSUPPORTED = 4, /* head_dim or head grouping not implemented */
+  BCA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  BCA_ERR_HIP = 6          /* the HIP runtime refused a launch */
+} bca_status_t;
+
+typedef enum { BCA_F32 = 0, BCA_BF16 = 1 } bca_dtype_t;
+
+/* Version of this ABI (BCA_ABI_VERSION of the built library). */
+int32_t bca_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* bca_status_string(int32_t status);
+
+/* Message describing the calling thread's most recent failure ("" if none).
+ * The string is owned by the library and valid until the next call from the
+ * same thread. */
+const char* bca_last_error(void);
+
+/*
+ * Block-causal forward over packed variable-length sequences.
+ *   q, k, v     : inputs (layouts above), element type `dtype`
+ *   o           : output [total, hq, d], element type `dtype`
+ *   lse         : output [hq, total] float32
+ *   cu_seqlens  : device int32 [nseq + 1]
+ *   nseq        : number of segments (>= 0; 0 enqueues nothing)
+ *   max_seqlen  : an upper bound on every segment length (> 0 when total > 0)
+ *   total       : number of packed tokens (cu_seqlens[nseq])
+ *   hq, hkv, d  : query heads, KV heads, head_dim; d in {64, 128}
+ *   block_size  : B >= 1
+ *   scale       : multiplies q.k before the softmax (typically 1/sqrt(d))
+ * Every row of o and lse for the `total` tokens is written.
+ * Equivalent to bca_staircase_fwd with s_copies = NULL.
+ */
+bca_status_t bca_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens, int32_t nseq, int32_t max_seqlen,
+                     int32_t total, int32_t hq, int32_t hkv, int32_t d, int32_t block_size,
+                     float scale, bca_dtype_t dtype, void* stream);
+
+/*
+ * Staircase packed-replay forward.  As bca_fwd, plus
+ *   s_copies : device int32 [nseq], copies S of the last block per segment
+ *              (NULL = no copies, i.e. plain block-causal).
+ */
+bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void* o,
+                               float* lse, const int32_t* cu_seqlens, const int32_t* s_copies,
+                               int32_t nseq, int32_t max_seqlen, int32_t total, int32_t hq,
+                               int32_t hkv, int32_t d, int32_t block_size, float scale,
+                               bca_dtype_t dtype, void* stream);
+
+/* Bytes of workspace bca_staircase_bwd needs: a float32 dQ accumulator
+ * [total, hq, d] and the float32 row terms rowsum(dO * O) [hq, total]. */
+size_t bca_staircase_bwd_workspace(int32_t total, int32_t hq, int32_t hkv, int32_t d);
+
+/*
+ * Staircase (and, with s_copies = NULL, block-causal) backward, bf16 only.
+ *   q, k, v, o, lse : the forward's inputs and outputs (o and lse exactly as
+ *                     produced by bca_staircase_fwd for the same inputs)
+ *   dout            : dO [total, hq, d] bf16
+ *   dq              : output [total, hq, d] bf16
+ *   dk, dv          : outputs [total, hkv, d] bf16, summed over the hq/hkv
+ *                     query heads that share each KV head
+ *   workspace       : device buffer of at least
+ *                     bca_staircase_bwd_workspace(total, hq, hkv, d) bytes;
+ *                     contents undefined on entry and on exit
+ * Other arguments as bca_staircase_fwd.
+ */
+bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk,
+                               void* dv, const int32_t* cu_seqlens, const int32_t* s_copies,
+                               int32_t nseq, int32_t max_seqlen, int32_t total, int32_t hq,
+                               int32_t hkv, int32_t d, int32_t block_size, float scale,
+                               bca_dtype_t dtype, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+/* Bytes of workspace bca_decode needs for `num_splits` key chunks
+ * (num_splits = 0: the count bca_decode would choose itself).  Returns 0 for
+ * invalid sizes. */
+size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                            int32_t num_splits);
+
+/*
+ * Decode step: one block of q_len noisy queries against a KV cache, bf16 only.
+ *   q          : [q_len, hq, d] bf16 (the current block's queries)
+ *   k, v       : [kv_len, hkv, d] bf16; rows [0, kv_len - q_len) are the prefix
+ *                cache and the last q_len rows the block's own keys/values
+ *   o          : output [q_len, hq, d] bf16
+ *   lse        : output [hq, q_len] float32
+ *   num_splits : number of key chunks processed in parallel (split-KV) and
+ *                merged by log-sum-exp weights; 0 = chosen by the library
+ *   workspace  : device buffer of at least
+ *                bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
+ *                bytes (may be NULL when that size is 0); contents undefined
+ *                on entry and on exit
+ * Every query attends to all kv_len keys (no mask).
+ */
+bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                        float scale, bca_dtype_t dtype, int32_t num_splits, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCA_H */

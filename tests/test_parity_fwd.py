@@ -1,0 +1,109 @@
+"""GPU parity of the forward kernels (block-causal and staircase) with the oracle.
+
+Small problems are compared element by element on every row; the full-size
+workloads on sampled rows (segment and block edges, the prefix/copy boundary
+and random rows) that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_lm_causal_amd import bca
+from block_diffusion_lm_causal_amd import workloads as W
+
+from gpu_helpers import (TOL_BF16, TOL_F32, device_inputs, max_abs, oracle_rows, run_fwd,
+                         sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(w, tol):
+    o, lse = run_fwd(w)
+    O, LSE = oracle.attention_fwd(w.q, w.k, w.v, w.cu_seqlens, w.s_copies, w.block_size, w.scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    eo, el = max_abs(o, O), max_abs(lse, LSE)
+    print(f"{w.name}: max|dO| = {eo:.3g}, max|dLSE| = {el:.3g}")
+    assert eo <= tol, eo
+    assert el <= tol, el
+
+
+def test_fp32_block_causal_L256_d64():
+    full_check(W.blockcausal_fp32_small(), TOL_F32)
+
+
+SMALL = [
+    # name, seqlens, copies, hq, hkv, d, B, dtype
+    ("ragged_L200_gqa4", [200], [0], 4, 1, 128, 32, "bf16"),
+    ("packed_with_empty_d64", [77, 0, 130, 64], [0, 0, 0, 0], 8, 2, 64, 16, "bf16"),
+    ("causal_B1", [300], [0], 2, 2, 128, 1, "bf16"),
+    ("full_B_eq_L_mha", [150], [0], 3, 3, 64, 150, "bf16"),
+    ("B_gt_L", [90], [0], 4, 2, 128, 128, "bf16"),
+    ("staircase_two_traj", [96 + 5 * 32, 32 + 3 * 32], [5, 3], 32, 8, 128, 32, "bf16"),
+    ("staircase_no_prefix", [4 * 32], [4], 8, 8, 128, 32, "bf16"),
+    ("staircase_B64_group8", [64 * 3 + 2 * 64], [2], 16, 2, 128, 64, "bf16"),
+    ("staircase_B8_group2", [40 + 3 * 8, 8 * 9 + 7 * 8], [3, 7], 6, 3, 64, 8, "bf16"),
+    ("odd_B7_group3", [1000], [0], 12, 4, 128, 7, "bf16"),
+    ("single_token", [1, 1, 2], [0, 0, 0], 4, 4, 128, 32, "bf16"),
+    ("f32_packed_gqa", [200, 57], [0, 0], 4, 2, 128, 16, "f32"),
+    ("f32_staircase", [40 + 3 * 8], [3], 2, 1, 64, 8, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases(case):
+    name, seqlens, copies, hq, hkv, d, B, dt = case
+    w = W.packed(name, "staircase_fwd", 100 + len(name), seqlens, copies, hq, hkv, d, B, dt)
+    full_check(w, TOL_F32 if dt == "f32" else TOL_BF16)
+
+
+def test_block_causal_entry_equals_staircase_without_copies():
+    w = W.packed("bc", "fwd", 7, [333, 64], [0, 0], 8, 2, 128, 32, "bf16")
+    o1, l1 = run_fwd(w, staircase=True)
+    o2, l2 = run_fwd(w, staircase=False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def sampled_check(w, seed):
+    rng = np.random.default_rng(seed)
+    o, lse = run_fwd(w)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = sample_rows(w, rng)
+    O, LSE = oracle_rows(w, rows)
+    eo = max_abs(o[rows], O[rows])
+    el = max_abs(lse[:, rows], LSE[:, rows])
+    print(f"{w.name}: {len(rows)} rows x {w.hq} heads, max|dO| = {eo:.3g}, max|dLSE| = {el:.3g}")
+    assert eo <= TOL_BF16, eo
+    assert el <= TOL_BF16, el
+
+
+def test_prefill_4k_sampled():
+    sampled_check(W.prefill_bf16_4k(), 1)
+
+
+def test_staircase_8traj_sampled():
+    sampled_check(W.staircase_fwd_8traj(), 3)
+
+
+def test_staircase_16traj_forward_sampled():
+    sampled_check(W.staircase_bwd_16traj(), 4)
+
+
+def test_forward_is_deterministic():
+    w = W.prefill_bf16_4k()
+    q, k, v, cu, sc, _ = device_inputs(w)
+    o1, l1 = bca.fwd(q, k, v, cu, w.block_size, w.scale, w.max_seqlen)
+    o2, l2 = bca.fwd(q, k, v, cu, w.block_size, w.scale, w.max_seqlen)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_every_row_written():
+    # Outputs pre-filled with NaN must come back finite on every row.
+    w = W.staircase_fwd_8traj()
+    q, k, v, cu, sc, _ = device_inputs(w)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.hq, w.total), float("nan"), device=q.device)
+    bca.staircase_fwd(q, k, v, cu, sc, w.block_size, w.scale, w.max_seqlen, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
