@@ -137,9 +137,8 @@ bca_status_t bca_fwd(const void* q, const void* k, const void* v, void* o, float
 
 size_t bca_staircase_bwd_workspace(int32_t total, int32_t hq, int32_t hkv, int32_t d) {
   if (total < 0 || hq <= 0 || hkv <= 0 || d <= 0) return 0;
-  const size_t dq = (size_t)total * hq * d * sizeof(float);
   const size_t delta = (size_t)hq * total * sizeof(float);
-  return ((dq + 255) & ~(size_t)255) + ((delta + 255) & ~(size_t)255);
+  return (delta + 255) & ~(size_t)255;
 }
 
 bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -172,9 +171,7 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  const size_t dq_bytes = ((size_t)total * hq * d * sizeof(float) + 255) & ~(size_t)255;
-  a.dq_acc = static_cast<float*>(workspace);
-  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + dq_bytes);
+  a.delta = static_cast<float*>(workspace);
   a.cu_seqlens = cu_seqlens;
   a.s_copies = s_copies;
   a.nseq = nseq;

@@ -57,8 +57,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;      // [total, hq, d] float32 workspace
-  float* delta;       // [hq, total] float32 workspace
+  float* delta;       // [hq, total] float32 workspace: rowsum(dO * O)
   const int32_t* cu_seqlens;
   const int32_t* s_copies;
   int nseq, total, hq, hkv, d, block_size;
