@@ -12,19 +12,26 @@
 // of one query head; the workgroup's waves are `hpw` query heads that share a
 // KV head (GQA) times 4/hpw consecutive 32-row sub-tiles, so K/V tiles staged
 // in LDS serve all of them.  The workgroup walks only the key tiles its rows
-// admit (whole masked tiles are never issued), 64 keys at a time, with
-// double-buffered LDS and the next tile's global loads in flight while the
-// current tile is multiplied.
+// admit (whole masked tiles are never issued), 64 keys at a time.
 //
-// Per 64-key tile each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
-// (keys on the M axis, its 32 queries on the N axis), so every lane holds 32
-// scores of a single query: the row max needs one cross-lane step (lane^32)
-// and the running sum stays lane-local until the epilogue.  Probabilities are
-// rounded to bf16 and fed straight back as the B operand of O^T += V^T P^T;
-// V is stored transposed in LDS with the key order inside each 16-key chunk
-// permuted to match the accumulator layout of S^T, so no register shuffles are
-// needed between the two products.  Softmax runs in the log2 domain
-// (scale * log2(e) folded into one multiply, exp2 on v_exp_f32).
+// Data movement.  K and V tiles go from HBM straight into LDS
+// (buffer_load ... lds, 16 bytes per lane), double-buffered, with the next
+// tile in flight while the current one is multiplied.  The buffer resource of
+// each tile ends at the tile's last valid key, so rows past it arrive as zeros
+// without any per-lane work.  Tiles are stored row-major with a 16-byte chunk
+// swizzle (bca_device.hpp) that keeps both LDS read patterns conflict-free.
+//
+// Math.  Per 64-key tile each wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (keys on M, its 32 queries on N, Q held in
+// registers), so each lane holds 32 scores of one query: the row max needs a
+// single cross-lane step (lane ^ 32) and the row sum stays lane-local until
+// the epilogue.  Probabilities are rounded to bf16 and fed back unchanged as
+// the B operand of O^T += V^T P^T; the V^T operand comes from the row-major V
+// tile through the transposed LDS read (ds_read_b64_tr_b16), in the key order
+// the S^T accumulator already has.  Softmax runs in the log2 domain: one FMA
+// applies scale * log2(e) and subtracts the running max before v_exp_f32.
+// The running max is only moved (and O rescaled) when a row's maximum grows
+// by more than 2^8, which keeps P <= 256 and skips almost every rescale.
 #include "bca_device.hpp"
 #include "bca_kernels.hpp"
 
@@ -34,85 +41,49 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBN = 64;    // keys per tile
 constexpr int kRows = 32;  // query rows per wave
+constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before rescaling
 
+// K tiles are double-buffered; V tiles triple-buffered because P V of a tile
+// runs one iteration after its Q K^T (see attend()).
 template <int D>
 struct Lds {
-  static constexpr int kKPitch = D + 8;    // bf16 per K row  (row = 68 dwords for D = 128)
-  static constexpr int kVPitch = kBN + 8;  // bf16 per V^T row (row = 36 dwords)
-  uint16_t k[2][kBN * kKPitch];
-  uint16_t vt[2][D * kVPitch];
+  uint16_t k[2][kBN * D];
+  uint16_t v[3][kBN * D];
 };
 
-// Position, inside a 16-key chunk of the V^T tile, of key kk (bits 2 and 3
-// swapped): lane half 0 of the S^T accumulator holds keys {0-3, 8-11} of every
-// 16-key chunk and lane half 1 keys {4-7, 12-15}.
-__device__ __forceinline__ int vt_pos(int key) {
-  int kk = key & 15;
-  return (key & ~15) | (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
+// Direct HBM -> LDS loads of one K and one V tile.
 template <int D>
 struct TileLoader {
-  // K: BN*D/8 16-byte chunks, D/8 per key row.  V: (BN/4)*(D/8) items of
-  // 4 keys x 8 dims, transposed into V^T on the way into LDS.
-  static constexpr int kKChunks = kBN * D / 8 / kThreads;          // per thread
-  static constexpr int kVItems = (kBN / 4) * (D / 8);              // total
-  static constexpr int kVPerThread = (kVItems + kThreads - 1) / kThreads;
-  u32x4 kr[kKChunks];
-  u32x4 vr[kVPerThread][4];
+  static constexpr int kChunks = D / 8;                      // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;          // rows one instruction fills
+  static constexpr int kInstPerWave = kBN / kRowsPerInst / 4;
+  uint32_t voff[kInstPerWave];  // per-lane byte offset inside the tile
+  int lds_row0[kInstPerWave];   // first row written by each instruction (wave-uniform)
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ kbase,
-                                       const uint16_t* __restrict__ vbase, int row_stride,
-                                       int k0, int kend, int tid) {
+  __device__ __forceinline__ void init(int row_bytes, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int i = 0; i < kKChunks; ++i) {
-      int id = tid + i * kThreads;
-      int key = id / (D / 8), ch = id % (D / 8);
-      int j = k0 + key;
-      if (j < kend) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * row_stride + ch * 8);
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kVPerThread; ++i) {
-      int item = tid + i * kThreads;
-      int m = item % (kBN / 4), ch = item / (kBN / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int j = k0 + 4 * m + e;
-        if (item < kVItems && j < kend) {
-          vr[i][e] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * row_stride + ch * 8);
-        } else {
-          vr[i][e] = u32x4{0, 0, 0, 0};
-        }
-      }
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const int row0 = (i * 4 + wave) * kRowsPerInst;
+      const int R = row0 + lane / kChunks;
+      const int c = (lane % kChunks) ^ swz<D>(R);  // logical chunk landing in this lane's slot
+      voff[i] = (uint32_t)(R * row_bytes + c * 16);
+      lds_row0[i] = row0;
     }
   }
 
-  __device__ __forceinline__ void store(Lds<D>& lds, int buf, int tid) {
+  // keys [k0, min(k0 + 64, kend)) of rows with byte stride row_bytes
+  __device__ __forceinline__ void issue(const uint16_t* kb, const uint16_t* vb, int row_elems,
+                                        int k0, int kend, Lds<D>& lds, int kbuf, int vbuf) {
+    // only rows [0, 64) of the tile are ever read, so the range never needs more
+    const int rows = min(kend - k0, kBN);
+    const uint32_t nbytes = (uint32_t)((rows - 1) * row_elems * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * row_elems, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_elems, nbytes);
 #pragma unroll
-    for (int i = 0; i < kKChunks; ++i) {
-      int id = tid + i * kThreads;
-      int key = id / (D / 8), ch = id % (D / 8);
-      *reinterpret_cast<u32x4*>(&lds.k[buf][key * Lds<D>::kKPitch + ch * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kVPerThread; ++i) {
-      int item = tid + i * kThreads;
-      if (item < kVItems) {
-        int m = item % (kBN / 4), ch = item / (kBN / 4);
-        int pos = vt_pos(4 * m);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          int w = dd >> 1, sh = (dd & 1) * 16;
-          uint32_t lo = ((vr[i][0][w] >> sh) & 0xffffu) | (((vr[i][1][w] >> sh) & 0xffffu) << 16);
-          uint32_t hi = ((vr[i][2][w] >> sh) & 0xffffu) | (((vr[i][3][w] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<u32x2*>(&lds.vt[buf][(ch * 8 + dd) * Lds<D>::kVPitch + pos]) =
-              u32x2{lo, hi};
-        }
-      }
+    for (int i = 0; i < kInstPerWave; ++i) {
+      buffer_load_lds16(rk, &lds.k[kbuf][lds_row0[i] * D], voff[i]);
+      buffer_load_lds16(rv, &lds.v[vbuf][lds_row0[i] * D], voff[i]);
     }
   }
 };
@@ -123,10 +94,8 @@ struct WgPlan {
   const uint16_t* k;     // key rows of the segment, already offset to the KV head
   const uint16_t* v;
   int q_rows;            // valid query rows (segment length, or q_len for decode)
-  int q0;                // first query row of the workgroup tile
   int r1s, r1e, r2s, r2e;  // key ranges to visit
-  int P, L, B;           // admitted-key rule (decode: P = L = key end, everything admitted)
-  int head_wave;         // query head of the calling wave
+  int P, L, B;           // admitted-key rule (decode: every key below the chunk end)
   int qw0;               // first query row of the calling wave
 };
 
@@ -136,6 +105,25 @@ struct WaveState {
   float m;             // running max (log2 domain), identical in lanes l and l^32
   float l;             // lane-local partial running sum
 };
+
+// O^T += V^T P^T for one 64-key tile: V^T fragments through the transposed LDS
+// read, P^T as the B operand straight from the S^T accumulator layout.
+template <int D>
+__device__ __forceinline__ void pv_update(const char* vt, const uint32_t (&voff)[D / 32][2],
+                                          const uint32_t (&pk)[kBN / 16][4], WaveState<D>& ws) {
+#pragma unroll
+  for (int c = 0; c < kBN / 16; ++c) {
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const s16x4 lo = lds_read_tr16(vt + voff[dt][0] + c * 16 * D * 2);
+      const s16x4 hi = lds_read_tr16(vt + voff[dt][1] + c * 16 * D * 2);
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+      ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.acc[dt], 0, 0, 0);
+    }
+  }
+}
 
 // The tile loop: accumulates softmax(scale * q K^T) V over the planned key
 // ranges into ws (unnormalised, with running max and partial sums).
@@ -148,6 +136,13 @@ __device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_str
   const int qi = p.qw0 + (lane & 31);
   const bool wave_active = p.qw0 < p.q_rows;
   const int qw_last = min(p.qw0 + kRows, p.q_rows) - 1;
+
+  TileLoader<D> ld;
+  ld.init(kv_stride * 2, tid);
+  const int n1 = (p.r1e - p.r1s + kBN - 1) / kBN;
+  const int n2 = p.r2e > p.r2s ? (p.r2e - p.r2s + kBN - 1) / kBN : 0;
+  const int ntile = n1 + n2;
+  if (ntile > 0) ld.issue(p.k, p.v, kv_stride, p.r1s, p.r1e, lds, 0, 0);
 
   // Query fragments: B operand of S^T = K Q^T, 8 consecutive dims per lane.
   bf16x8 qf[D / 16];
@@ -167,38 +162,65 @@ __device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_str
   const int s2_first = (qw_last >= p.P) ? row_keys(first_copy_row, p.P, p.L, p.B).s2 : 0x7fffffff;
   const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
 
+  // Per-lane LDS byte offsets inside a tile.
+  // K (A operand of S^T): row lane%32 (+32 for the second key half), logical chunk 2kk + half.
+  uint32_t koff[D / 16];
+  {
+    const int s = swz<D>(lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      koff[kk] = (uint32_t)((lane & 31) * D * 2 + (((2 * kk + half) ^ s) * 16));
+  }
+  // V (A operand of O^T, transposed read): 16-lane group G, address-lane 4r + q reads
+  // rows 16c + 8sub + 4half + r, dims 32dt + 16(G%2) + 4q.
+  uint32_t voff[D / 32][2];
+  {
+    const int a = lane & 15, r = a >> 2, q = a & 3, g2 = (lane >> 4) & 1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = 8 * sub + 4 * half + r;
+        const int chunk = 4 * dt + 2 * g2 + (q >> 1);
+        voff[dt][sub] = (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
+      }
+    }
+  }
+
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
   ws.m = kNegBig;
   ws.l = 0.f;
-
-  const int n1 = (p.r1e - p.r1s + kBN - 1) / kBN;
-  const int n2 = p.r2e > p.r2s ? (p.r2e - p.r2s + kBN - 1) / kBN : 0;
-  const int ntile = n1 + n2;
   if (ntile == 0) return;
 
-  TileLoader<D> ld;
-  ld.load(p.k, p.v, kv_stride, p.r1s, p.r1e, tid);
-  ld.store(lds, 0, tid);
+  wait_vmem();
   __syncthreads();
 
+  // Software pipeline: iteration t runs O^T += V^T P^T for tile t-1 (no loads in
+  // flight, so the transposed V reads never wait on memory), then puts tile t+1
+  // in flight, then computes S^T and P for tile t.
+  uint32_t pk[kBN / 16][4];  // P^T of the previous tile, bf16 pairs
+  bool pv_pending = false;
+  int vbuf_prev = 0, vbuf = 0;
   for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
-    const int k0 = t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN;
-    const int kend = t < n1 ? p.r1e : p.r2e;
+    if (pv_pending) pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
+    const int kbuf = t & 1;
+    const int vbuf_next = vbuf == 2 ? 0 : vbuf + 1;
     if (t + 1 < ntile) {
       const int t1 = t + 1;
-      const int k0n = t1 < n1 ? p.r1s + t1 * kBN : p.r2s + (t1 - n1) * kBN;
-      const int kendn = t1 < n1 ? p.r1e : p.r2e;
-      ld.load(p.k, p.v, kv_stride, k0n, kendn, tid);
+      ld.issue(p.k, p.v, kv_stride, t1 < n1 ? p.r1s + t1 * kBN : p.r2s + (t1 - n1) * kBN,
+               t1 < n1 ? p.r1e : p.r2e, lds, kbuf ^ 1, vbuf_next);
     }
-
+    const int k0 = t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN;
+    const int kend = t < n1 ? p.r1e : p.r2e;
     const bool skip = !wave_active ||
                       (k0 >= rkB.e1 && (k0 + kBN <= s2_first || k0 >= rkB.e2));
+    pv_pending = !skip;
     if (!skip) {
       const bool full = (k0 + kBN <= kend) &&
                         ((k0 + kBN <= rkA.e1) ||
                          (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+      const char* kt = reinterpret_cast<const char*>(lds.k[kbuf]);
       // S^T tile: two 32-key halves.
       f32x16 s[kBN / 32];
 #pragma unroll
@@ -207,66 +229,64 @@ __device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_str
       for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
         for (int h = 0; h < kBN / 32; ++h) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &lds.k[buf][(h * 32 + (lane & 31)) * Lds<D>::kKPitch + kk * 16 + half * 8]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
           s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
         }
       }
-      // Scale, mask, row max.
+      // Mask (partial tiles only) and row max of the raw scores.
+      if (!full) {
+#pragma unroll
+        for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+            s[h][r] = ok ? s[h][r] : kNegInf;
+          }
+        }
+      }
       float mloc = kNegInf;
 #pragma unroll
       for (int h = 0; h < kBN / 32; ++h) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[h][r] * scale_log2;
-          if (!full) {
-            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (!(j < kend && admitted(rk, j))) x = kNegInf;
-          }
-          s[h][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
+        for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(s[h][r], s[h][r + 1]));
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(ws.m, mloc);
-      const float alpha = fast_exp2(ws.m - m_new);
-      ws.m = m_new;
-      float lsum = 0.f;
-      uint32_t pk[kBN / 16][4];
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+      // Move the running max only when some row outgrew it by the slack.
+      if (__builtin_amdgcn_ballot_w64(mloc > ws.m + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(ws.m, mloc);
+        const float alpha = fast_exp2(ws.m - m_new);
+        ws.m = m_new;
+        ws.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha;
+      }
+      const float neg_m = -ws.m;
+      float lsum = ws.l;
 #pragma unroll
       for (int h = 0; h < kBN / 32; ++h) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(s[h][r] - m_new);
-          const float p1 = fast_exp2(s[h][r + 1] - m_new);
-          lsum += p0 + p1;
+          const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
+          const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
+          lsum += p0 + p1;  // float32 sum of the unrounded probabilities
           pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
         }
       }
-      ws.l = ws.l * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int c = 0; c < kBN / 16; ++c) {
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &lds.vt[buf][(dt * 32 + (lane & 31)) * Lds<D>::kVPitch + c * 16 + half * 8]);
-          ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.acc[dt], 0, 0, 0);
-        }
-      }
+      ws.l = lsum;
     }
-    if (t + 1 < ntile) ld.store(lds, buf ^ 1, tid);
+    vbuf_prev = vbuf;
+    vbuf = vbuf_next;
+    wait_vmem();
     __syncthreads();
   }
+  if (pv_pending) pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
 }
 
 // Write the normalised rows of a wave: O as bf16 (or float32 partials) and LSE.
 template <int D, bool PARTIAL>
-__device__ __forceinline__ void write_rows(const WaveState<D>& ws, int qi, bool valid,
-                                           void* o_row, float* lse_out) {
+__device__ __forceinline__ void write_rows(const WaveState<D>& ws, bool valid, void* o_row,
+                                           float* lse_out) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const float l = ws.l + __shfl_xor(ws.l, 32);
@@ -288,7 +308,6 @@ __device__ __forceinline__ void write_rows(const WaveState<D>& ws, int qi, bool 
     }
   }
   if (half == 0) *lse_out = (ws.m + fast_log2(l)) * kLn2;
-  (void)qi;
 }
 
 template <int D>
@@ -313,19 +332,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const int wave = threadIdx.x >> 6;
   const int head = hg * a.hpw + wave % a.hpw;
-  const int g = head / (a.hq / a.hkv);
-  const int kv_head_wg = (hg * a.hpw) / (a.hq / a.hkv);
-  (void)g;
+  const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
   const int q0 = tile * tok;
   const int q_last = min(q0 + tok, L) - 1;
   const TileKeys tk = tile_keys(q0, q_last, P, L, a.block_size);
 
   WgPlan p;
   p.q = a.q + (size_t)base * a.hq * D + (size_t)head * D;
-  p.k = a.k + (size_t)base * a.hkv * D + (size_t)kv_head_wg * D;
-  p.v = a.v + (size_t)base * a.hkv * D + (size_t)kv_head_wg * D;
+  p.k = a.k + (size_t)base * a.hkv * D + (size_t)kv_head * D;
+  p.v = a.v + (size_t)base * a.hkv * D + (size_t)kv_head * D;
   p.q_rows = L;
-  p.q0 = q0;
   p.r1s = 0;
   p.r1e = tk.r1e;
   p.r2s = tk.r2s;
@@ -333,7 +349,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   p.P = P;
   p.L = L;
   p.B = a.block_size;
-  p.head_wave = head;
   p.qw0 = q0 + (wave / a.hpw) * kRows;
 
   WaveState<D> ws;
@@ -341,9 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int qi = p.qw0 + (lane & 31);
-  const bool valid = qi < L;
-  write_rows<D, false>(ws, qi, valid,
-                       a.o + ((size_t)(base + qi) * a.hq + head) * D,
+  write_rows<D, false>(ws, qi < L, a.o + ((size_t)(base + qi) * a.hq + head) * D,
                        a.lse + (size_t)head * a.total + base + qi);
 }
 
@@ -361,24 +374,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(DecodeArgs a) 
 
   const int wave = threadIdx.x >> 6;
   const int head = hg * a.hpw + wave % a.hpw;
-  const int kv_head_wg = (hg * a.hpw) / (a.hq / a.hkv);
+  const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
   const int kbeg = split * a.chunk;
   const int kend = min(a.kv_len, kbeg + a.chunk);
 
   WgPlan p;
   p.q = a.q + (size_t)head * D;
-  p.k = a.k + (size_t)kv_head_wg * D;
-  p.v = a.v + (size_t)kv_head_wg * D;
+  p.k = a.k + (size_t)kv_head * D;
+  p.v = a.v + (size_t)kv_head * D;
   p.q_rows = a.q_len;
-  p.q0 = tile * tok;
   p.r1s = kbeg;
   p.r1e = kend;
   p.r2s = p.r2e = 0;
   p.P = kend;  // every query row admits every key below the chunk end
   p.L = kend;
   p.B = 0x40000000;
-  p.head_wave = head;
-  p.qw0 = p.q0 + (wave / a.hpw) * kRows;
+  p.qw0 = tile * tok + (wave / a.hpw) * kRows;
 
   WaveState<D> ws;
   attend<D>(p, a.hq * D, a.hkv * D, a.scale_log2, lds, ws);
@@ -387,11 +398,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(DecodeArgs a) 
   const int qi = p.qw0 + (lane & 31);
   const bool valid = qi < a.q_len;
   if (a.nsplit == 1) {
-    write_rows<D, false>(ws, qi, valid, a.o + ((size_t)qi * a.hq + head) * D,
+    write_rows<D, false>(ws, valid, a.o + ((size_t)qi * a.hq + head) * D,
                          a.lse + (size_t)head * a.q_len + qi);
   } else {
-    write_rows<D, true>(ws, qi, valid,
-                        a.part_o + (((size_t)split * a.q_len + qi) * a.hq + head) * D,
+    write_rows<D, true>(ws, valid, a.part_o + (((size_t)split * a.q_len + qi) * a.hq + head) * D,
                         a.part_lse + ((size_t)split * a.hq + head) * a.q_len + qi);
   }
 }

@@ -33,6 +33,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, y);
 }
 
+// LDS address-space pointer types for the direct-to-LDS and transposed-read builtins.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ lds_void* as_lds(void* p) { return (lds_void*)(p); }
+
+// Buffer resource over [base, base + nbytes): loads at or past nbytes return zero.
+// Word 3 holds the data-format bits of a raw (untyped, stride 0) buffer on gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from buffer `r` at byte offset voffset into LDS at
+// lds_base + 16 * lane (lanes write consecutive 16-byte slots).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, as_lds(lds_base), 16, voffset, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// direct-to-LDS loads) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// if address-lane 4r + q points at element [row0 + r][col0 + 4q] of a
+// row-major 16-bit matrix, lane c receives rows row0..row0+3 of column
+// col0 + c.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// 16-byte chunk swizzle of a row-major tile with D/8 chunks per row: chunk c
+// of row r is stored at chunk c ^ swz(r).  Chosen so that 16 consecutive rows
+// read at one logical chunk, and 4 consecutive rows read at 4 consecutive
+// chunks through the transposed read, both hit distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
