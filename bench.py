@@ -79,8 +79,15 @@ def timed_calls(fn, steps: int, warmup: int, flush=None):
     timed region).  With flush, the cache-flush write runs before every timed call,
     outside its events, and the wall figure is not meaningful."""
     import torch
-    for _ in range(warmup):
+    # W warm-up calls, continued until about a second of work has run so the GPU
+    # clocks have settled before the timed region.
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or (time.perf_counter() - t_warm < 1.0 and done < 20 * max(warmup, 1)):
         fn()
+        done += 1
+        if done % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]

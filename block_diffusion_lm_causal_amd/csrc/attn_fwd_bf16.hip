@@ -61,7 +61,7 @@ struct TileLoader {
   int lds_row0[kInstPerWave];   // first row written by each instruction (wave-uniform)
 
   __device__ __forceinline__ void init(int row_bytes, int tid) {
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < kInstPerWave; ++i) {
       const int row0 = (i * 4 + wave) * kRowsPerInst;
@@ -192,18 +192,37 @@ __device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_str
   ws.m = kNegBig;
   ws.l = 0.f;
   if (ntile == 0) return;
+  {
+    // V buffer 2 stands in for "the tile before the first one": zeros.
+    u32x4* z = reinterpret_cast<u32x4*>(lds.v[2]);
+#pragma unroll
+    for (int i = 0; i < kBN * D * 2 / 16 / kThreads; ++i) z[tid + i * kThreads] = u32x4{0, 0, 0, 0};
+  }
 
   wait_vmem();
   __syncthreads();
 
-  // Software pipeline: iteration t runs O^T += V^T P^T for tile t-1 (no loads in
-  // flight, so the transposed V reads never wait on memory), then puts tile t+1
-  // in flight, then computes S^T and P for tile t.
+  // Software pipeline.  Iteration t computes S^T and the softmax of tile t and,
+  // interleaved with those exponentials, O^T += V^T P^T of tile t-1 (independent
+  // work, so MFMA and VALU overlap inside the wave).  Tile t+1 is put in flight
+  // at the top of the iteration.  A rescale of O (rare) is applied after the
+  // P V of tile t-1 has been accumulated against the old maximum.  Tile t uses V
+  // buffer t % 3; before the first tile the "previous" buffer (2) holds zeros
+  // and P is zero, so the loop body needs no first-iteration branch.  A wave
+  // whose rows admit no key of a tile runs it fully masked (P = 0).
   uint32_t pk[kBN / 16][4];  // P^T of the previous tile, bf16 pairs
-  bool pv_pending = false;
-  int vbuf_prev = 0, vbuf = 0;
+#pragma unroll
+  for (int c = 0; c < kBN / 16; ++c) pk[c][0] = pk[c][1] = pk[c][2] = pk[c][3] = 0u;
+  int vbuf_prev = 2, vbuf = 0;
+  float alpha_prev = 1.f;     // rescale decided by the previous tile, not yet applied to O
+  bool rescale_prev = false;  // wave-uniform
   for (int t = 0; t < ntile; ++t) {
-    if (pv_pending) pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
+    // O must be rescaled after the P V of tile t-2 (done last iteration) and
+    // before that of tile t-1 (done below).
+    if (rescale_prev) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
+    }
     const int kbuf = t & 1;
     const int vbuf_next = vbuf == 2 ? 0 : vbuf + 1;
     if (t + 1 < ntile) {
@@ -211,76 +230,96 @@ __device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_str
       ld.issue(p.k, p.v, kv_stride, t1 < n1 ? p.r1s + t1 * kBN : p.r2s + (t1 - n1) * kBN,
                t1 < n1 ? p.r1e : p.r2e, lds, kbuf ^ 1, vbuf_next);
     }
+    const char* vprev = reinterpret_cast<const char*>(lds.v[vbuf_prev]);
     const int k0 = t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN;
     const int kend = t < n1 ? p.r1e : p.r2e;
-    const bool skip = !wave_active ||
-                      (k0 >= rkB.e1 && (k0 + kBN <= s2_first || k0 >= rkB.e2));
-    pv_pending = !skip;
-    if (!skip) {
-      const bool full = (k0 + kBN <= kend) &&
-                        ((k0 + kBN <= rkA.e1) ||
-                         (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
-      const char* kt = reinterpret_cast<const char*>(lds.k[kbuf]);
-      // S^T tile: two 32-key halves.
-      f32x16 s[kBN / 32];
+    const bool full = wave_active && (k0 + kBN <= kend) &&
+                      ((k0 + kBN <= rkA.e1) ||
+                       (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+    const char* kt = reinterpret_cast<const char*>(lds.k[kbuf]);
+    // S^T tile: two 32-key halves.
+    f32x16 s[kBN / 32];
 #pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
+    for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-        for (int h = 0; h < kBN / 32; ++h) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
-        }
+      for (int h = 0; h < kBN / 32; ++h) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
       }
-      // Mask (partial tiles only) and row max of the raw scores.
-      if (!full) {
-#pragma unroll
-        for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
-            s[h][r] = ok ? s[h][r] : kNegInf;
-          }
-        }
-      }
-      float mloc = kNegInf;
+    }
+    // Mask (partial tiles only).
+    if (!full) {
 #pragma unroll
       for (int h = 0; h < kBN / 32; ++h) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(s[h][r], s[h][r + 1]));
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
-      // Move the running max only when some row outgrew it by the slack.
-      if (__builtin_amdgcn_ballot_w64(mloc > ws.m + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(ws.m, mloc);
-        const float alpha = fast_exp2(ws.m - m_new);
-        ws.m = m_new;
-        ws.l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha;
-      }
-      const float neg_m = -ws.m;
-      float lsum = ws.l;
-#pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
-          const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
-          lsum += p0 + p1;  // float32 sum of the unrounded probabilities
-          pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+          s[h][r] = ok ? s[h][r] : kNegInf;
         }
       }
-      ws.l = lsum;
+    }
+    // Row max, softmax of tile t, interleaved with P V of tile t-1.
+    // tree reduction (short dependency chain), then the other half-wave
+    float mt[kBN / 4];
+#pragma unroll
+    for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
+    }
+#pragma unroll
+    for (int w = kBN / 8; w >= 1; w >>= 1) {
+#pragma unroll
+      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
+    }
+    const float mloc = xhalf_max(mt[0]) * scale_log2;
+    // Move a row's running max only when the row outgrew it by the slack (a
+    // per-lane select: no branch splits the softmax from the P V MFMAs below).
+    const bool grow = mloc > ws.m + kRescaleSlack;
+    const float m_new = grow ? mloc : ws.m;
+    const float alpha = fast_exp2(ws.m - m_new);
+    ws.m = m_new;
+    const float neg_m = -m_new;
+    float lsum = ws.l * alpha;
+    uint32_t pn[kBN / 16][4];
+#pragma unroll
+    for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
+        lsum += p0 + p1;  // float32 sum of the unrounded probabilities
+        pn[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    }
+    ws.l = lsum;
+    pv_update<D>(vprev, voff, pk, ws);
+    // Issue order hint: two transposed V reads, one MFMA, then softmax VALU work.
+#pragma unroll
+    for (int i = 0; i < (kBN / 16) * (D / 32); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+    rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
+    alpha_prev = alpha;
+#pragma unroll
+    for (int c = 0; c < kBN / 16; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[c][e] = pn[c][e];
     }
     vbuf_prev = vbuf;
     vbuf = vbuf_next;
     wait_vmem();
     __syncthreads();
   }
-  if (pv_pending) pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
+  if (rescale_prev) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
+  }
+  pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
 }
 
 // Write the normalised rows of a wave: O as bf16 (or float32 partials) and LSE.
@@ -289,7 +328,7 @@ __device__ __forceinline__ void write_rows(const WaveState<D>& ws, bool valid, v
                                            float* lse_out) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  const float l = ws.l + __shfl_xor(ws.l, 32);
+  const float l = xhalf_sum(ws.l);
   const float inv = 1.f / l;
   if (!valid) return;
 #pragma unroll
@@ -308,6 +347,258 @@ __device__ __forceinline__ void write_rows(const WaveState<D>& ws, bool valid, v
     }
   }
   if (half == 0) *lse_out = (ws.m + fast_log2(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong forward: 8 waves in two groups of 4 (A = waves 0-3, B = waves 4-7,
+// one wave of each group per SIMD).  Both groups consume the same K/V tiles;
+// B runs one phase behind A, so on every SIMD one wave is in an MFMA phase
+// (S^T of tile t and O^T += V^T P^T of tile t-1) while the other is in its
+// softmax phase (VALU), and they swap at each barrier.  Phase phi:
+//   A: phi even -> MFMA(phi/2), phi odd -> softmax((phi-1)/2)
+//   B: the same with phi - 1.
+// At even phi = 2t every wave issues its share of the loads of K(t+1) and V(t)
+// (double buffers for both), which complete by the end of phase 2t+1.
+
+constexpr int kPPThreads = 512;
+
+template <int D>
+struct LdsPP {
+  uint16_t k[2][kBN * D];
+  uint16_t v[2][kBN * D];
+};
+
+template <int D>
+struct PPLoader {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRowsPerInst = 64 / kChunks;
+  static constexpr int kInstPerWave = kBN / kRowsPerInst / 8;  // per tensor
+  uint32_t voff[kInstPerWave];
+  int lds_row0[kInstPerWave];
+
+  __device__ __forceinline__ void init(int row_bytes, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const int row0 = (i * 8 + wave) * kRowsPerInst;
+      const int R = row0 + lane / kChunks;
+      const int c = (lane % kChunks) ^ swz<D>(R);
+      voff[i] = (uint32_t)(R * row_bytes + c * 16);
+      lds_row0[i] = row0;
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t* base, int row_elems, int k0, int kend,
+                                        uint16_t* dst) {
+    const int rows = min(kend - k0, kBN);
+    const uint32_t nbytes = (uint32_t)((rows - 1) * row_elems * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)k0 * row_elems, nbytes);
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) buffer_load_lds16(r, dst + lds_row0[i] * D, voff[i]);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_stride,
+                                          float scale_log2, LdsPP<D>& lds, WaveState<D>& ws) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: A, 1: B (one phase behind)
+  const int qi = p.qw0 + (lane & 31);
+  const bool wave_active = p.qw0 < p.q_rows;
+  const int qw_last = min(p.qw0 + kRows, p.q_rows) - 1;
+
+  PPLoader<D> ld;
+  ld.init(kv_stride * 2, wave, lane);
+  const int n1 = (p.r1e - p.r1s + kBN - 1) / kBN;
+  const int n2 = p.r2e > p.r2s ? (p.r2e - p.r2s + kBN - 1) / kBN : 0;
+  const int ntile = n1 + n2;
+  auto tile_k0 = [&](int t) { return t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN; };
+  auto tile_end = [&](int t) { return t < n1 ? p.r1e : p.r2e; };
+  if (ntile > 0) ld.issue(p.k, kv_stride, tile_k0(0), tile_end(0), lds.k[0]);
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 raw = u32x4{0, 0, 0, 0};
+    if (qi < p.q_rows) {
+      raw = *reinterpret_cast<const u32x4*>(p.q + (size_t)qi * q_stride + kk * 16 + half * 8);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+  }
+  const RowKeys rk = row_keys(qi < p.q_rows ? qi : qw_last, p.P, p.L, p.B);
+  const RowKeys rkA = row_keys(p.qw0 < p.q_rows ? p.qw0 : 0, p.P, p.L, p.B);
+  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, p.P, p.L, p.B);
+  const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
+
+  uint32_t koff[D / 16];
+  {
+    const int sw = swz<D>(lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      koff[kk] = (uint32_t)((lane & 31) * D * 2 + (((2 * kk + half) ^ sw) * 16));
+  }
+  uint32_t voff[D / 32][2];
+  {
+    const int a = lane & 15, r = a >> 2, q = a & 3, g2 = (lane >> 4) & 1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = 8 * sub + 4 * half + r;
+        const int chunk = 4 * dt + 2 * g2 + (q >> 1);
+        voff[dt][sub] = (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
+  ws.m = kNegBig;
+  ws.l = 0.f;
+  if (ntile == 0) return;
+  wait_vmem();
+  __syncthreads();
+
+  f32x16 s[kBN / 32];         // S^T of the tile between its MFMA and softmax phases
+  uint32_t pk[kBN / 16][4];   // P^T of the tile between its softmax and P V phases
+  float alpha_prev = 1.f;
+  bool rescale_prev = false;
+  const int nphase = 2 * ntile + 2;
+  for (int phi = 0; phi < nphase; ++phi) {
+    if ((phi & 1) == 0) {
+      const int t = phi >> 1;
+      if (t + 1 < ntile) ld.issue(p.k, kv_stride, tile_k0(t + 1), tile_end(t + 1), lds.k[(t + 1) & 1]);
+      if (t < ntile) ld.issue(p.v, kv_stride, tile_k0(t), tile_end(t), lds.v[t & 1]);
+    }
+    const int my = phi - grp;
+    if (my >= 0 && (my & 1) == 0) {
+      // MFMA phase for tile tm: rescale pending from softmax(tm-1), P V of
+      // tile tm-1, then S^T of tile tm.
+      const int tm = my >> 1;
+      if (rescale_prev) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
+      }
+      if (tm >= 1) {
+        pv_update<D>(reinterpret_cast<const char*>(lds.v[(tm - 1) & 1]), voff, pk, ws);
+      }
+      if (tm < ntile) {
+        const char* kt = reinterpret_cast<const char*>(lds.k[tm & 1]);
+#pragma unroll
+        for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+          for (int h = 0; h < kBN / 32; ++h) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
+            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
+          }
+        }
+      }
+    } else if (my >= 0 && (my >> 1) < ntile) {
+      // Softmax phase for tile tv.
+      const int tv = my >> 1;
+      const int k0 = tile_k0(tv), kend = tile_end(tv);
+      const bool full = wave_active && (k0 + kBN <= kend) &&
+                        ((k0 + kBN <= rkA.e1) ||
+                         (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+      if (!full) {
+#pragma unroll
+        for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+            s[h][r] = ok ? s[h][r] : kNegInf;
+          }
+        }
+      }
+      float mt[kBN / 4];
+#pragma unroll
+      for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
+      }
+#pragma unroll
+      for (int w = kBN / 8; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
+      }
+      const float mloc = xhalf_max(mt[0]) * scale_log2;
+      const bool grow = mloc > ws.m + kRescaleSlack;
+      const float m_new = grow ? mloc : ws.m;
+      const float alpha = fast_exp2(ws.m - m_new);
+      ws.m = m_new;
+      const float neg_m = -m_new;
+      float lsum = ws.l * alpha;
+#pragma unroll
+      for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
+          const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
+          lsum += p0 + p1;
+          pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        }
+      }
+      ws.l = lsum;
+      rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
+      alpha_prev = alpha;
+    }
+    if (phi & 1) wait_vmem();
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
+  __shared__ LdsPP<D> lds;
+  const int ngroups = a.hq / a.hpw;
+  const int tok = kRows * (8 / a.hpw);
+  const int w = blockIdx.x;
+  const int hg = w % ngroups;
+  const int rest = w / ngroups;
+  const int seg = rest % a.nseq;
+  const int rank = rest / a.nseq;
+
+  const int base = a.cu_seqlens[seg];
+  const int L = a.cu_seqlens[seg + 1] - base;
+  const int ntiles = (L + tok - 1) / tok;
+  if (rank >= ntiles) return;
+  const int tile = ntiles - 1 - rank;
+  const int S = a.s_copies ? a.s_copies[seg] : 0;
+  int P = L - S * a.block_size;
+  if (P < 0) P = 0;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int head = hg * a.hpw + wave % a.hpw;
+  const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
+  const int q0 = tile * tok;
+  const int q_last = min(q0 + tok, L) - 1;
+  const TileKeys tk = tile_keys(q0, q_last, P, L, a.block_size);
+
+  WgPlan p;
+  p.q = a.q + (size_t)base * a.hq * D + (size_t)head * D;
+  p.k = a.k + (size_t)base * a.hkv * D + (size_t)kv_head * D;
+  p.v = a.v + (size_t)base * a.hkv * D + (size_t)kv_head * D;
+  p.q_rows = L;
+  p.r1s = 0;
+  p.r1e = tk.r1e;
+  p.r2s = tk.r2s;
+  p.r2e = tk.r2e;
+  p.P = P;
+  p.L = L;
+  p.B = a.block_size;
+  p.qw0 = q0 + (wave / a.hpw) * kRows;
+
+  WaveState<D> ws;
+  attend_pp<D>(p, a.hq * D, a.hkv * D, a.scale_log2, lds, ws);
+
+  const int lane = threadIdx.x & 63;
+  const int qi = p.qw0 + (lane & 31);
+  write_rows<D, false>(ws, qi < L, a.o + ((size_t)(base + qi) * a.hq + head) * D,
+                       a.lse + (size_t)head * a.total + base + qi);
 }
 
 template <int D>
@@ -330,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   int P = L - S * a.block_size;
   if (P < 0) P = 0;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head = hg * a.hpw + wave % a.hpw;
   const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
   const int q0 = tile * tok;
@@ -372,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(DecodeArgs a) 
   const int tile = rest % ntok;
   const int split = rest / ntok;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head = hg * a.hpw + wave % a.hpw;
   const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
   const int kbeg = split * a.chunk;
@@ -449,14 +740,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int ntiles_max, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const FwdArgs& a, int max_seqlen, hipStream_t stream) {
   const int ngroups = a.hq / a.hpw;
-  const long long nwg = (long long)ntiles_max * a.nseq * ngroups;
+  const int tok = kRows * (8 / a.hpw);  // query tokens per 8-wave workgroup
+  const long long ntiles = (max_seqlen + tok - 1) / tok;
+  const long long nwg = ntiles * a.nseq * ngroups;
   if (nwg <= 0) return hipSuccess;
   if (a.d == 128) {
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(fwd_pp_kernel<128>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(fwd_pp_kernel<64>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -105,9 +105,7 @@ bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void
     a.block_size = block_size;
     a.hpw = bca::heads_per_wg(hq, hkv);
     a.scale_log2 = scale * kLog2e;
-    const int tok = 32 * (4 / a.hpw);
-    const int ntiles = (max_seqlen + tok - 1) / tok;
-    return hip_status(bca::launch_fwd_bf16(a, ntiles, s), "forward launch");
+    return hip_status(bca::launch_fwd_bf16(a, max_seqlen, s), "forward launch");
   }
   bca::FwdF32Args a;
   a.q = static_cast<const float*>(q);

@@ -74,7 +74,7 @@ inline int heads_per_wg(int hq, int hkv) {
   return 1;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int ntiles_max, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int max_seqlen, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdF32Args& a, int max_seqlen, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream);
