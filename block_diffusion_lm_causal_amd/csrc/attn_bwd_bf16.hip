@@ -11,37 +11,31 @@
 // and P is recomputed from Q, K and the forward's LSE.
 //
 // Three kernels, no atomics (results are bit-reproducible):
-//   1. delta = rowsum(dO * O) in float32, one row per 16 lanes.
-//   2. dK/dV: a workgroup owns 128 keys of one KV head (32 per wave), keeps
-//      its K and V fragments in registers and its dK, dV accumulators in
-//      registers, and sweeps every 32-row query tile of every query head of
-//      the group that admits any of its keys.  S = Q K^T is computed with
-//      queries on the M axis so that the accumulators of P and dS are,
-//      unchanged, the A operands of dV += P^T dO and dK += dS^T Q (queries
-//      permuted inside each 16-row chunk, matched by the transposed dO and Q
-//      tiles staged in LDS).
-//   3. dQ: shaped like the forward -- a workgroup owns 32 query rows of up to
-//      four query heads sharing a KV head and sweeps the admitted key tiles;
-//      S^T = K Q^T and dP^T = V dO^T put one query per lane, so dS^T is the B
-//      operand of dQ^T += K^T dS^T with K^T staged in LDS.
+//   1. delta = rowsum(dO * O) in float32.
+//   2. dK/dV: an 8-wave workgroup owns 128 keys of one KV head.  Waves 0-3
+//      ("V waves", 32 keys each) compute S = Q K^T -> P -> dV += P^T dO;
+//      waves 4-7 ("K waves", the same keys) compute S and dP = dO V^T ->
+//      dS -> dK += dS^T Q.  Each SIMD pairs one wave of each kind, so one's
+//      MFMA work overlaps the other's exponentials.  K and V fragments and the
+//      dK/dV accumulators stay in registers; each step streams a 32-row tile
+//      of Q and dO (one query head) through LDS, loaded straight from HBM two
+//      steps ahead.  S is computed with queries on the M axis, so the P and dS
+//      accumulators are, unchanged, the A operands of the dV and dK products;
+//      their B operands (dO and Q with queries on K) come from the row-major
+//      tiles through the transposed LDS read.
+//   3. dQ: shaped like the forward's ping-pong kernel -- two groups of four
+//      waves, one phase apart, over 64-key tiles: MFMA phase S^T(t) = K Q^T,
+//      dP^T(t) = V dO^T and dQ^T += K^T dS^T(t-1); VALU phase P and dS of
+//      tile t.  K^T comes from the row-major K tile through the transposed read.
 #include "bca_device.hpp"
 #include "bca_kernels.hpp"
 
 namespace bca {
 namespace {
 
-constexpr int kThreads = 256;
-
-__device__ __forceinline__ int perm16(int idx) {
-  // bits 2 and 3 swapped: order of rows/keys inside a 16-chunk that matches
-  // the register order of a 32x32 MFMA accumulator's lane halves.
-  int kk = idx & 15;
-  return (idx & ~15) | (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
-
-__device__ __forceinline__ uint32_t bf16_pair(uint32_t a, uint32_t b, int sh) {
-  return ((a >> sh) & 0xffffu) | (((b >> sh) & 0xffffu) << 16);
-}
+constexpr int kBN = 32;    // keys per tile in the dQ kernel
+constexpr int kQt = 32;    // query rows per dK/dV step
+constexpr int kKvKeys = 128;  // keys per dK/dV workgroup
 
 // ---------------------------------------------------------------------------
 // 1. delta[h][i] = sum_d dO[i,h,d] * O[i,h,d]
@@ -70,82 +64,51 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 }
 
+// s_waitcnt vmcnt(n) for small n (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// A operand fragment of a row-major swizzled tile: row lane%32 (+ row_base),
+// logical 16-byte chunk 2kk + half.
+template <int D>
+__device__ __forceinline__ uint32_t row_frag_off(int lane, int kk) {
+  const int half = lane >> 5;
+  return (uint32_t)((lane & 31) * D * 2 + (((2 * kk + half) ^ swz<D>(lane & 15)) * 16));
+}
+
+// Transposed-read offsets: 16-lane group G, address-lane 4r + q reads rows
+// 8sub + 4half + r (of a 16-row chunk), columns 32dt + 16(G%2) + 4q.
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(int lane, int dt, int sub) {
+  const int half = lane >> 5;
+  const int a = lane & 15, r = a >> 2, q = a & 3, g2 = (lane >> 4) & 1;
+  const int row = 8 * sub + 4 * half + r;
+  const int chunk = 4 * dt + 2 * g2 + (q >> 1);
+  return (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lds_read_tr16(p0));
+  const u32x2 h2 = __builtin_bit_cast(u32x2, lds_read_tr16(p1));
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
 // ---------------------------------------------------------------------------
 // 2. dK / dV
 
-constexpr int kKvKeys = 128;  // keys per workgroup (32 per wave)
-constexpr int kQt = 32;       // query rows per tile
-
 template <int D>
 struct KvLds {
-  static constexpr int kRowPitch = D + 8;   // bf16, row-major [32][D]
-  static constexpr int kTPitch = kQt + 8;   // bf16, transposed [D][32] (queries permuted)
-  uint16_t q[2][kQt * kRowPitch];
-  uint16_t qt[2][D * kTPitch];
-  uint16_t g[2][kQt * kRowPitch];   // dO
-  uint16_t gt[2][D * kTPitch];
-  float lse2[2][kQt];   // LSE * log2(e)
-  float delta[2][kQt];
-};
-
-// One (query tile, head) step's global loads: item = 4 rows x 8 dims of Q or dO.
-template <int D>
-struct QTileLoader {
-  static constexpr int kItems = (kQt / 4) * (D / 8);  // per tensor: 128 (D=128) or 64
-  u32x4 r[4];
-  float side;  // lse or delta of one row (threads < 2 * kQt)
-
-  __device__ __forceinline__ void load(const BwdArgs& a, int base, int L, int qt0, int head,
-                                       int tid) {
-    const int tensor = tid / kItems;  // 0: Q, 1: dO, >= 2 idle (D = 64)
-    const int item = tid % kItems;
-    const int m = item % (kQt / 4), ch = item / (kQt / 4);
-    const uint16_t* src = tensor == 0 ? a.q : a.dout;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = qt0 + 4 * m + e;
-      if (tensor < 2 && i < L) {
-        r[e] = *reinterpret_cast<const u32x4*>(src + ((size_t)(base + i) * a.hq + head) * D + ch * 8);
-      } else {
-        r[e] = u32x4{0, 0, 0, 0};
-      }
-    }
-    side = 0.f;
-    if (tid < 2 * kQt) {
-      const int i = qt0 + (tid % kQt);
-      if (i < L) {
-        side = tid < kQt ? a.lse[(size_t)head * a.total + base + i] * kLog2e
-                         : a.delta[(size_t)head * a.total + base + i];
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(KvLds<D>& s, int buf, int tid) {
-    const int tensor = tid / kItems;
-    const int item = tid % kItems;
-    const int m = item % (kQt / 4), ch = item / (kQt / 4);
-    if (tensor < 2) {
-      uint16_t* rowm = tensor == 0 ? s.q[buf] : s.g[buf];
-      uint16_t* tr = tensor == 0 ? s.qt[buf] : s.gt[buf];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<u32x4*>(&rowm[(4 * m + e) * KvLds<D>::kRowPitch + ch * 8]) = r[e];
-      }
-      const int pos = perm16(4 * m);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1, sh = (dd & 1) * 16;
-        *reinterpret_cast<u32x2*>(&tr[(ch * 8 + dd) * KvLds<D>::kTPitch + pos]) =
-            u32x2{bf16_pair(r[0][w], r[1][w], sh), bf16_pair(r[2][w], r[3][w], sh)};
-      }
-    }
-    if (tid < kQt) s.lse2[buf][tid] = side;
-    else if (tid < 2 * kQt) s.delta[buf][tid - kQt] = side;
-  }
+  uint16_t q[3][kQt * D];    // Q tile, row-major swizzled
+  uint16_t g[3][kQt * D];    // dO tile
+  float lse2[3][kQt];        // LSE * log2(e) of the tile's rows
+  float delta[3][kQt];
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ KvLds<D> lds;
   const int group = a.hq / a.hkv;
   const int w = blockIdx.x;
@@ -165,9 +128,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;
-  const int wave = tid >> 6;
-  const int kw0 = k0 + wave * 32;           // this wave's first key
-  const int key = kw0 + (lane & 31);        // key of this lane's B-operand column
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool kwave = wave >= 4;           // K waves compute dK, V waves dV
+  const int kw0 = k0 + (wave & 3) * 32;   // this wave's first key
+  const int key = kw0 + (lane & 31);      // key of this lane's accumulator column
   const int k_last_wg = min(k0 + kKvKeys, L) - 1;
 
   // Query rows that admit any key of the workgroup.
@@ -180,8 +144,68 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     qs = P + c_first * B;
     qe = min(L, P + (c_last + 1) * B);
   }
+  const int nqt = (qe - qs + kQt - 1) / kQt;
+  const int nsteps = nqt * group;
 
-  // K and V fragments (B operands of S = Q K^T and dP = dO V^T) stay in registers.
+  // Loads: Q and dO tiles (32 rows x D) by DMA.  A tile is kInstPerTile
+  // 1 KB instructions per tensor; instruction i of the 2 * kInstPerTile is
+  // issued by wave i % 8 (Q blocks first, then dO blocks).  LSE/delta rows are
+  // loaded by wave 0 with plain loads.
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunks;               // 4 (D=128) or 8 (D=64)
+  constexpr int kInstPerTile = kQt / kRowsPerInst;         // 8 or 4
+  constexpr int kDmaPerWave = 2 * kInstPerTile / 8;        // 2 or 1 per step
+  const int q_row_elems = a.hq * D;
+  uint32_t dma_voff[kDmaPerWave];
+  int dma_row0[kDmaPerWave];
+  bool dma_is_q[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int i = wave + 8 * j;
+    dma_is_q[j] = i < kInstPerTile;
+    dma_row0[j] = (dma_is_q[j] ? i : i - kInstPerTile) * kRowsPerInst;
+    const int R = dma_row0[j] + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz<D>(R);
+    dma_voff[j] = (uint32_t)(R * q_row_elems * 2 + c * 16);
+  }
+  auto issue_step = [&](int st, int buf) {
+    const int qt0 = qs + (st / group) * kQt;
+    const int head = g * group + st % group;
+    const int rows = min(qe - qt0, kQt);
+    const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
+    const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + off, nbytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + off, nbytes);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      if (dma_is_q[j]) buffer_load_lds16(rq, &lds.q[buf][dma_row0[j] * D], dma_voff[j]);
+      else buffer_load_lds16(rg, &lds.g[buf][dma_row0[j] * D], dma_voff[j]);
+    }
+  };
+  // Wait until only the newest step's loads may be outstanding (wave 0 also
+  // has its LSE/delta load in that step).
+  auto wait_all_but_newest = [&]() {
+    if (wave == 0) wait_vmem_le<kDmaPerWave + 1>();
+    else wait_vmem_le<kDmaPerWave>();
+  };
+  auto load_side = [&](int st) -> float {
+    // wave 0: lanes 0-31 the LSE of the tile's rows (scaled by log2 e), 32-63 delta
+    const int qt0 = qs + (st / group) * kQt;
+    const int head = g * group + st % group;
+    const int i = qt0 + (lane & 31);
+    float v = 0.f;
+    if (i < qe) {
+      v = half == 0 ? a.lse[(size_t)head * a.total + base + i] * kLog2e
+                    : a.delta[(size_t)head * a.total + base + i];
+    }
+    return v;
+  };
+  auto store_side = [&](float v, int buf) {
+    if (half == 0) lds.lse2[buf][lane] = v;
+    else lds.delta[buf][lane & 31] = v;
+  };
+
+  // K and V fragments of this wave's keys (B operands of S = Q K^T and dP = dO V^T).
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -189,47 +213,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (key < L) {
       const size_t off = ((size_t)(base + key) * a.hkv + g) * D + kk * 16 + half * 8;
       rk = *reinterpret_cast<const u32x4*>(a.k + off);
-      rv = *reinterpret_cast<const u32x4*>(a.v + off);
+      if (kwave) rv = *reinterpret_cast<const u32x4*>(a.v + off);
     }
     kf[kk] = __builtin_bit_cast(bf16x8, rk);
     vf[kk] = __builtin_bit_cast(bf16x8, rv);
   }
+  f32x16 acc[D / 32];  // dV (V waves) or dK (K waves): keys on M, dims on N
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  f32x16 dk[D / 32], dv[D / 32];
+  uint32_t roff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) roff[kk] = row_frag_off<D>(lane, kk);
+  uint32_t toff[D / 32][2];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    dk[dt] = f32x16{};
-    dv[dt] = f32x16{};
+    toff[dt][0] = tr_off<D>(lane, dt, 0);
+    toff[dt][1] = tr_off<D>(lane, dt, 1);
   }
 
   const int wave_key_last = min(kw0 + 31, L - 1);
   const bool wave_has_keys = kw0 < L;
-  const int nqt = (qe - qs + kQt - 1) / kQt;
-  const int nsteps = nqt * group;
 
-  QTileLoader<D> ld;
+  // Prologue: steps 0 and 1 in flight, step 0's side values in LDS.
+  float side_next = 0.f, side_new = 0.f;
   if (nsteps > 0) {
-    ld.load(a, base, qe, qs, g * group, tid);
-    ld.store(lds, 0, tid);
+    if (wave == 0) store_side(load_side(0), 0);
+    issue_step(0, 0);
+    if (nsteps > 1) {
+      if (wave == 0) side_next = load_side(1);
+      issue_step(1, 1);
+    }
   }
+  if (nsteps > 1) wait_all_but_newest();  // step 0's tile landed (step 1's may remain)
+  else wait_vmem();
   __syncthreads();
 
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    const int qt0 = qs + (st / group) * kQt;
-    if (st + 1 < nsteps) {
-      const int st1 = st + 1;
-      ld.load(a, base, qe, qs + (st1 / group) * kQt, g * group + st1 % group, tid);
+    const int buf = st % 3;
+    if (st + 2 < nsteps) {
+      if (wave == 0) side_new = load_side(st + 2);
+      issue_step(st + 2, (st + 2) % 3);
     }
-
+    const int qt0 = qs + (st / group) * kQt;
     // Does any row of this query tile admit any key of this wave?
     const int qa = qt0, qb = min(qt0 + kQt, qe) - 1;
     const RowKeys ra = row_keys(qa, P, L, B);
     const RowKeys rb = row_keys(qb, P, L, B);
     bool active = wave_has_keys;
     if (active) {
-      // rows admit prefix keys up to e1 (non-decreasing in the row) and,
-      // for copy rows, their own copy
       const bool hits_prefix = kw0 < rb.e1;
       const int first_copy_row = qa > P ? qa : P;
       const bool hits_copy = qb >= P && kw0 < rb.e2 &&
@@ -237,64 +269,80 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       active = hits_prefix || hits_copy;
     }
     if (active) {
-      // every (row, key) of the tile admitted: no padding rows or keys, and the
-      // keys inside the prefix part all rows see, or inside the one copy they share
       const bool full = qt0 + kQt <= qe && kw0 + 31 < L &&
                         ((kw0 + 31 < ra.e1) ||
                          (ra.e2 > ra.s2 && ra.s2 == rb.s2 && kw0 >= ra.s2 && kw0 + 31 < ra.e2));
-      // S = Q K^T and dP = dO V^T, queries on M, keys on N.
+      const char* qtile = reinterpret_cast<const char*>(lds.q[buf]);
+      const char* gtile = reinterpret_cast<const char*>(lds.g[buf]);
+      // S = Q K^T (and dP = dO V^T in K waves): queries on M, keys on N.
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(
-            &lds.q[buf][(lane & 31) * KvLds<D>::kRowPitch + kk * 16 + half * 8]);
-        const bf16x8 ga8 = *reinterpret_cast<const bf16x8*>(
-            &lds.g[buf][(lane & 31) * KvLds<D>::kRowPitch + kk * 16 + half * 8]);
+        const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qtile + roff[kk]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kf[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga8, vf[kk], dp, 0, 0, 0);
       }
-      // P and dS; accumulator register r holds query row 8(r/4) + 4 half + r%4.
-      uint32_t pp[2][4], pds[2][4];
+      if (kwave) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float pv[2], dsv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int qr = 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-          const float l2 = lds.lse2[buf][qr];
-          const float dl = lds.delta[buf][qr];
-          float p = fast_exp2(s[r + e] * a.scale_log2 - l2);
-          if (!full) {
-            const int i = qt0 + qr;
-            if (!(i < qe && key < L && admitted(row_keys(i, P, L, B), key))) p = 0.f;
-          }
-          pv[e] = p;
-          dsv[e] = p * (dp[r + e] - dl);
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 ga8 = *reinterpret_cast<const bf16x8*>(gtile + roff[kk]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga8, vf[kk], dp, 0, 0, 0);
         }
-        pp[r >> 3][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
-        pds[r >> 3][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
       }
-      // dV += P^T dO and dK += dS^T Q: keys on M, dims on N, queries contracted.
+      // P (and dS); register r holds query row 8(r/4) + 4 half + r%4.
+      uint32_t pk[2][4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int q0r = 8 * r4 + 4 * half;
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&lds.lse2[buf][q0r]);
+        f32x4 dl = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kwave) dl = *reinterpret_cast<const f32x4*>(&lds.delta[buf][q0r]);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float pv = fast_exp2(fmaf(s[r], a.scale_log2, -l2[e]));
+          if (!full) {
+            const int i = qt0 + q0r + e;
+            const bool ok = (i < qe) & (key < L) & admitted(row_keys(i, P, L, B), key);
+            pv = ok ? pv : 0.f;
+          }
+          v[e] = kwave ? pv * (dp[r] - dl[e]) : pv;
+        }
+        pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
+        pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
+      }
+      // dV += P^T dO (V waves) or dK += dS^T Q (K waves): keys on M, dims on N,
+      // queries contracted; B operand through the transposed read.
+      const char* btile = kwave ? qtile : gtile;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pp[c][0], pp[c][1], pp[c][2], pp[c][3]});
-        const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{pds[c][0], pds[c][1], pds[c][2], pds[c][3]});
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const int row = (dt * 32 + (lane & 31)) * KvLds<D>::kTPitch + c * 16 + half * 8;
-          const bf16x8 gb = *reinterpret_cast<const bf16x8*>(&lds.gt[buf][row]);
-          const bf16x8 qb8 = *reinterpret_cast<const bf16x8*>(&lds.qt[buf][row]);
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qb8, dk[dt], 0, 0, 0);
+          const bf16x8 b8 = tr_pair(btile + toff[dt][0] + c * 16 * D * 2,
+                                    btile + toff[dt][1] + c * 16 * D * 2);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b8, acc[dt], 0, 0, 0);
         }
       }
     }
-    if (st + 1 < nsteps) ld.store(lds, buf ^ 1, tid);
+    // Step st+1's tile must have landed; step st+2's may still be in flight.
+    if (st + 2 < nsteps) {
+      if (wave == 0) {
+        store_side(side_next, (st + 1) % 3);
+        side_next = side_new;
+      }
+      wait_all_but_newest();
+    } else {
+      if (wave == 0 && st + 1 < nsteps) store_side(side_next, (st + 1) % 3);
+      wait_vmem();
+    }
     __syncthreads();
   }
 
   // Epilogue: lane holds dims 32 dt + lane%32 of keys 8(r/4) + 4 half + r%4.
   if (!wave_has_keys) return;
+  uint16_t* out = kwave ? a.dk : a.dv;
+  const float mul = kwave ? a.scale : 1.f;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -302,72 +350,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int kr = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (kr < L) {
         const size_t off = ((size_t)(base + kr) * a.hkv + g) * D + dt * 32 + (lane & 31);
-        a.dk[off] = static_cast<uint16_t>(pack_bf16x2(dk[dt][r] * a.scale, 0.f) & 0xffffu);
-        a.dv[off] = static_cast<uint16_t>(pack_bf16x2(dv[dt][r], 0.f) & 0xffffu);
+        out[off] = static_cast<uint16_t>(pack_bf16x2(acc[dt][r] * mul, 0.f) & 0xffffu);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ
-
-constexpr int kBN = 64;  // keys per tile
+// 3. dQ (ping-pong)
 
 template <int D>
 struct DqLds {
-  static constexpr int kKPitch = D + 8;
-  static constexpr int kTPitch = kBN + 8;
-  uint16_t k[2][kBN * kKPitch];
-  uint16_t v[2][kBN * kKPitch];
-  uint16_t kt[2][D * kTPitch];
+  uint16_t k[3][kBN * D];
+  uint16_t v[2][kBN * D];
 };
 
 template <int D>
-struct KvTileLoader {
-  // item = 4 keys x 8 dims of K and of V
-  static constexpr int kItems = (kBN / 4) * (D / 8);  // 256 (D=128) or 128
-  u32x4 kr[4], vr[4];
-
-  __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, int stride, int k0,
-                                       int kend, int tid) {
-    const int m = tid % (kBN / 4), ch = tid / (kBN / 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = k0 + 4 * m + e;
-      if (tid < kItems && j < kend) {
-        kr[e] = *reinterpret_cast<const u32x4*>(kb + (size_t)j * stride + ch * 8);
-        vr[e] = *reinterpret_cast<const u32x4*>(vb + (size_t)j * stride + ch * 8);
-      } else {
-        kr[e] = u32x4{0, 0, 0, 0};
-        vr[e] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(DqLds<D>& s, int buf, int tid) {
-    if (tid >= kItems) return;
-    const int m = tid % (kBN / 4), ch = tid / (kBN / 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<u32x4*>(&s.k[buf][(4 * m + e) * DqLds<D>::kKPitch + ch * 8]) = kr[e];
-      *reinterpret_cast<u32x4*>(&s.v[buf][(4 * m + e) * DqLds<D>::kKPitch + ch * 8]) = vr[e];
-    }
-    const int pos = perm16(4 * m);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int w = dd >> 1, sh = (dd & 1) * 16;
-      *reinterpret_cast<u32x2*>(&s.kt[buf][(ch * 8 + dd) * DqLds<D>::kTPitch + pos]) =
-          u32x2{bf16_pair(kr[0][w], kr[1][w], sh), bf16_pair(kr[2][w], kr[3][w], sh)};
-    }
-  }
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int hpw) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw) {
   __shared__ DqLds<D> lds;
   const int ngroups = a.hq / hpw;
-  const int tok = 32 * (4 / hpw);
+  const int tok = 32 * (8 / hpw);
   const int w = blockIdx.x;
   const int hg = w % ngroups;
   const int rest = w / ngroups;
@@ -375,9 +377,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int hpw)
   const int rank = rest / a.nseq;
   const int base = a.cu_seqlens[seg];
   const int L = a.cu_seqlens[seg + 1] - base;
-  const int ntiles = (L + tok - 1) / tok;
-  if (rank >= ntiles) return;
-  const int tile = ntiles - 1 - rank;
+  const int ntiles_q = (L + tok - 1) / tok;
+  if (rank >= ntiles_q) return;
+  const int tile = ntiles_q - 1 - rank;
   const int S = a.s_copies ? a.s_copies[seg] : 0;
   int P = L - S * a.block_size;
   if (P < 0) P = 0;
@@ -386,7 +388,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int hpw)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int head = hg * hpw + wave % hpw;
   const int g = (hg * hpw) / (a.hq / a.hkv);
   const int q0 = tile * tok;
@@ -396,6 +399,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int hpw)
   const int qi = qw0 + (lane & 31);
   const bool wave_active = qw0 < L;
   const int qw_last = min(qw0 + 32, L) - 1;
+
+  const int kv_elems = a.hkv * D;
+  const uint16_t* kb = a.k + (size_t)base * kv_elems + (size_t)g * D;
+  const uint16_t* vb = a.v + (size_t)base * kv_elems + (size_t)g * D;
+  const int n1 = (tk.r1e + kBN - 1) / kBN;
+  const int n2 = tk.r2e > tk.r2s ? (tk.r2e - tk.r2s + kBN - 1) / kBN : 0;
+  const int ntile = n1 + n2;
+  auto tile_k0 = [&](int t) { return t < n1 ? t * kBN : tk.r2s + (t - n1) * kBN; };
+  auto tile_end = [&](int t) { return t < n1 ? tk.r1e : tk.r2e; };
+
+  // DMA: a kBN x D tile is kBN*D*2/1024 instructions per tensor; wave w issues
+  // instruction w of each tensor (waves past the count issue none).
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunks;
+  constexpr int kInstPerTensor = kBN / kRowsPerInst;  // 8 (D=128) or 4 (D=64)
+  const bool dma_wave = wave < kInstPerTensor;
+  const int drow0 = wave * kRowsPerInst;
+  const uint32_t dvoff = [&] {
+    const int R = drow0 + lane / kChunks;
+    return (uint32_t)(R * kv_elems * 2 + (((lane % kChunks) ^ swz<D>(R)) * 16));
+  }();
+  auto issue = [&](const uint16_t* src, int t, uint16_t* dst) {
+    if (!dma_wave) return;
+    const int k0 = tile_k0(t);
+    const int rows = min(tile_end(t) - k0, kBN);
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(src + (size_t)k0 * kv_elems, (uint32_t)((rows - 1) * kv_elems * 2 + D * 2));
+    buffer_load_lds16(r, dst + drow0 * D, dvoff);
+  };
+  if (ntile > 0) {
+    issue(kb, 0, lds.k[0]);
+    issue(vb, 0, lds.v[0]);
+  }
 
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -417,87 +453,101 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a, int hpw)
   const RowKeys rk = row_keys(qi < L ? qi : qw_last, P, L, B);
   const RowKeys rkA = row_keys(wave_active ? qw0 : 0, P, L, B);
   const RowKeys rkB = row_keys(wave_active ? qw_last : 0, P, L, B);
-  const int first_copy_row = qw0 > P ? qw0 : P;
-  const int s2_first = (qw_last >= P) ? row_keys(first_copy_row, P, L, B).s2 : 0x7fffffff;
   const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
 
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) koff[kk] = row_frag_off<D>(lane, kk);
+  uint32_t toff[D / 32][2];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    toff[dt][0] = tr_off<D>(lane, dt, 0);
+    toff[dt][1] = tr_off<D>(lane, dt, 1);
+  }
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  const uint16_t* kb = a.k + (size_t)base * a.hkv * D + (size_t)g * D;
-  const uint16_t* vb = a.v + (size_t)base * a.hkv * D + (size_t)g * D;
-  const int n1 = (tk.r1e + kBN - 1) / kBN;
-  const int n2 = tk.r2e > tk.r2s ? (tk.r2e - tk.r2s + kBN - 1) / kBN : 0;
-  const int ntile = n1 + n2;
-
-  KvTileLoader<D> ld;
   if (ntile > 0) {
-    ld.load(kb, vb, a.hkv * D, 0, tk.r1e, tid);
-    ld.store(lds, 0, tid);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
-    const int k0 = t < n1 ? t * kBN : tk.r2s + (t - n1) * kBN;
-    const int kend = t < n1 ? tk.r1e : tk.r2e;
-    if (t + 1 < ntile) {
-      const int t1 = t + 1;
-      ld.load(kb, vb, a.hkv * D, t1 < n1 ? t1 * kBN : tk.r2s + (t1 - n1) * kBN,
-              t1 < n1 ? tk.r1e : tk.r2e, tid);
-    }
-    const bool skip = !wave_active || (k0 >= rkB.e1 && (k0 + kBN <= s2_first || k0 >= rkB.e2));
-    if (!skip) {
-      const bool full = (k0 + kBN <= kend) &&
-                        ((k0 + kBN <= rkA.e1) || (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
-      f32x16 s[kBN / 32], dp[kBN / 32];
-#pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
-        s[h] = f32x16{};
-        dp[h] = f32x16{};
+    wait_vmem();
+    __syncthreads();
+    f32x16 s[kBN / 32], dp[kBN / 32];
+    uint32_t pk[kBN / 16][4];  // dS^T of the tile between its VALU and dQ phases
+    const int nphase = 2 * ntile + 2;
+    for (int phi = 0; phi < nphase; ++phi) {
+      if ((phi & 1) == 0) {
+        const int t = phi >> 1;
+        if (t + 1 < ntile) {
+          issue(kb, t + 1, lds.k[(t + 1) % 3]);
+          issue(vb, t + 1, lds.v[(t + 1) & 1]);
+        }
       }
+      const int my = phi - grp;
+      if (my >= 0 && (my & 1) == 0) {
+        // MFMA phase for tile tm: dQ^T += K^T dS^T of tile tm-1, then S^T and dP^T of tm.
+        const int tm = my >> 1;
+        if (tm >= 1) {
+          const char* kt = reinterpret_cast<const char*>(lds.k[(tm - 1) % 3]);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+          for (int c = 0; c < kBN / 16; ++c) {
+            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+              const bf16x8 ka = tr_pair(kt + toff[dt][0] + c * 16 * D * 2,
+                                        kt + toff[dt][1] + c * 16 * D * 2);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db, acc[dt], 0, 0, 0);
+            }
+          }
+        }
+        if (tm < ntile) {
+          const char* kt = reinterpret_cast<const char*>(lds.k[tm % 3]);
+          const char* vt = reinterpret_cast<const char*>(lds.v[tm & 1]);
+#pragma unroll
+          for (int h = 0; h < kBN / 32; ++h) {
+            s[h] = f32x16{};
+            dp[h] = f32x16{};
+          }
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+            for (int h = 0; h < kBN / 32; ++h) {
+              const uint32_t off = koff[kk] + h * 32 * D * 2;
+              const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
+              const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
+              s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[h], 0, 0, 0);
+              dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp[h], 0, 0, 0);
+            }
+          }
+        }
+      } else if (my >= 0 && (my >> 1) < ntile) {
+        // VALU phase for tile tv: P^T and dS^T.
+        const int tv = my >> 1;
+        const int k0 = tile_k0(tv), kend = tile_end(tv);
+        const bool full = wave_active && (k0 + kBN <= kend) &&
+                          ((k0 + kBN <= rkA.e1) ||
+                           (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
 #pragma unroll
         for (int h = 0; h < kBN / 32; ++h) {
-          const int off = (h * 32 + (lane & 31)) * DqLds<D>::kKPitch + kk * 16 + half * 8;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&lds.k[buf][off]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(&lds.v[buf][off]);
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[h], 0, 0, 0);
-          dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp[h], 0, 0, 0);
-        }
-      }
-      uint32_t pk[kBN / 16][4];
 #pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
+          for (int r = 0; r < 16; r += 2) {
+            float dsv[2];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float dsv[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float p = fast_exp2(s[h][r + e] * a.scale_log2 - lse2);
-            if (!full) {
-              const int j = k0 + h * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-              if (!(j < kend && admitted(rk, j))) p = 0.f;
+            for (int e = 0; e < 2; ++e) {
+              float p = fast_exp2(fmaf(s[h][r + e], a.scale_log2, -lse2));
+              if (!full) {
+                const int j = k0 + h * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
+                const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+                p = ok ? p : 0.f;
+              }
+              dsv[e] = p * (dp[h][r + e] - dl);
             }
-            dsv[e] = p * (dp[h][r + e] - dl);
+            pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
           }
-          pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
         }
       }
-#pragma unroll
-      for (int c = 0; c < kBN / 16; ++c) {
-        const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-              &lds.kt[buf][(dt * 32 + (lane & 31)) * DqLds<D>::kTPitch + c * 16 + half * 8]);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db, acc[dt], 0, 0, 0);
-        }
-      }
+      if (phi & 1) wait_vmem();
+      __syncthreads();
     }
-    if (t + 1 < ntile) ld.store(lds, buf ^ 1, tid);
-    __syncthreads();
   }
 
   if (!(qi < L)) return;
@@ -532,9 +582,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     const long long nkt = (max_seqlen + kKvKeys - 1) / kKvKeys;
     const long long nwg = nkt * a.nseq * a.hkv;
     if (a.d == 128) {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a);
     } else {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -542,13 +592,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
   // 3. dQ
   {
     const int hpw = heads_per_wg(a.hq, a.hkv);
-    const int tok = 32 * (4 / hpw);
+    const int tok = 32 * (8 / hpw);
     const long long ntiles = (max_seqlen + tok - 1) / tok;
     const long long nwg = ntiles * a.nseq * (a.hq / hpw);
     if (a.d == 128) {
-      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a, hpw);
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw);
     } else {
-      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a, hpw);
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw);
     }
     return hipGetLastError();
   }
