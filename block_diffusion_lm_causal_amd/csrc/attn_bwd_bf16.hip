@@ -108,14 +108,18 @@ struct KvLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max) {
   __shared__ KvLds<D> lds;
   const int group = a.hq / a.hkv;
+  // Order: KV head fastest, then the key tiles of one segment (earliest keys,
+  // i.e. most query rows, first), then the next segment.  Every workgroup
+  // sweeps its query tiles from the last one down, so the workgroups resident
+  // on an XCD stream the same Q/dO rows at the same time and share them in L2.
   const int w = blockIdx.x;
   const int g = w % a.hkv;
   const int rest = w / a.hkv;
-  const int seg = rest % a.nseq;
-  const int ktile = rest / a.nseq;  // earliest keys (most query rows) first
+  const int ktile = rest % nkt_max;
+  const int seg = rest / nkt_max;
   const int base = a.cu_seqlens[seg];
   const int L = a.cu_seqlens[seg + 1] - base;
   const int k0 = ktile * kKvKeys;
@@ -168,8 +172,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int c = (lane % kChunks) ^ swz<D>(R);
     dma_voff[j] = (uint32_t)(R * q_row_elems * 2 + c * 16);
   }
+  auto step_qt0 = [&](int st) { return qs + (nqt - 1 - st / group) * kQt; };
   auto issue_step = [&](int st, int buf) {
-    const int qt0 = qs + (st / group) * kQt;
+    const int qt0 = step_qt0(st);
     const int head = g * group + st % group;
     const int rows = min(qe - qt0, kQt);
     const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto load_side = [&](int st) -> float {
     // wave 0: lanes 0-31 the LSE of the tile's rows (scaled by log2 e), 32-63 delta
-    const int qt0 = qs + (st / group) * kQt;
+    const int qt0 = step_qt0(st);
     const int head = g * group + st % group;
     const int i = qt0 + (lane & 31);
     float v = 0.f;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if (wave == 0) side_new = load_side(st + 2);
       issue_step(st + 2, (st + 2) % 3);
     }
-    const int qt0 = qs + (st / group) * kQt;
+    const int qt0 = step_qt0(st);
     // Does any row of this query tile admit any key of this wave?
     const int qa = qt0, qb = min(qt0 + kQt, qe) - 1;
     const RowKeys ra = row_keys(qa, P, L, B);
@@ -366,15 +371,16 @@ struct DqLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int ntiles_max) {
   __shared__ DqLds<D> lds;
   const int ngroups = a.hq / hpw;
   const int tok = 32 * (8 / hpw);
+  // Order as the forward: head group fastest, then one segment's query tiles.
   const int w = blockIdx.x;
   const int hg = w % ngroups;
   const int rest = w / ngroups;
-  const int seg = rest % a.nseq;
-  const int rank = rest / a.nseq;
+  const int rank = rest % ntiles_max;
+  const int seg = rest / ntiles_max;
   const int base = a.cu_seqlens[seg];
   const int L = a.cu_seqlens[seg + 1] - base;
   const int ntiles_q = (L + tok - 1) / tok;
@@ -582,9 +588,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     const long long nkt = (max_seqlen + kKvKeys - 1) / kKvKeys;
     const long long nwg = nkt * a.nseq * a.hkv;
     if (a.d == 128) {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a,
+                         (int)nkt);
     } else {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a,
+                         (int)nkt);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -596,9 +604,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     const long long ntiles = (max_seqlen + tok - 1) / tok;
     const long long nwg = ntiles * a.nseq * (a.hq / hpw);
     if (a.d == 128) {
-      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw);
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw,
+                         (int)ntiles);
     } else {
-      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw);
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a, hpw,
+                         (int)ntiles);
     }
     return hipGetLastError();
   }

@@ -552,15 +552,18 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
 }
 
 template <int D>
-__global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a, int ntiles_max) {
   __shared__ LdsPP<D> lds;
   const int ngroups = a.hq / a.hpw;
   const int tok = kRows * (8 / a.hpw);
+  // Workgroup order: head group fastest (one KV head per XCD when there are 8),
+  // then the tiles of one segment, costliest first, then the next segment --
+  // so the workgroups resident on an XCD share one segment's K/V in L2.
   const int w = blockIdx.x;
   const int hg = w % ngroups;
   const int rest = w / ngroups;
-  const int seg = rest % a.nseq;
-  const int rank = rest / a.nseq;
+  const int rank = rest % ntiles_max;
+  const int seg = rest / ntiles_max;
 
   const int base = a.cu_seqlens[seg];
   const int L = a.cu_seqlens[seg + 1] - base;
@@ -747,9 +750,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int max_seqlen, hipStream_t stream)
   const long long nwg = ntiles * a.nseq * ngroups;
   if (nwg <= 0) return hipSuccess;
   if (a.d == 128) {
-    hipLaunchKernelGGL(fwd_pp_kernel<128>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
+    hipLaunchKernelGGL(fwd_pp_kernel<128>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a,
+                       (int)ntiles);
   } else {
-    hipLaunchKernelGGL(fwd_pp_kernel<64>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
+    hipLaunchKernelGGL(fwd_pp_kernel<64>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a,
+                       (int)ntiles);
   }
   return hipGetLastError();
 }
