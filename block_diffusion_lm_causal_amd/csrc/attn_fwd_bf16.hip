@@ -654,91 +654,339 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
                        a.lse + (size_t)head * a.total + base + qi);
 }
 
+// ---------------------------------------------------------------------------
+// Decode step: one workgroup per (KV head group, 32-token tile, key chunk).
+// Eight waves in two groups of four hold the same query rows (the hpw heads of
+// a KV head x 32 tokens); for every 64-key tile group A takes keys 0-31 and
+// group B keys 32-63, so both groups work on each tile as soon as it lands.
+// Up to kDecTiles tiles of the chunk are requested from HBM at once, each
+// wave issuing its share tile by tile; tile t becomes readable once every wave
+// has seen its own loads for tiles <= t complete (vmcnt) and passed a barrier,
+// while later tiles are still in flight.  The two groups merge their
+// (max, sum, O) through LDS at the end; the result is the final O and LSE
+// (one chunk) or a float32 partial that the combine kernel merges by
+// log-sum-exp weights.
+
+constexpr int kDecTiles = 5;  // key tiles of a chunk staged in LDS at once
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(DecodeArgs a) {
-  __shared__ Lds<D> lds;
+struct LdsDec {
+  uint16_t k[kDecTiles][kBN * D];
+  uint16_t v[kDecTiles][kBN * D];
+};
+
+// s_waitcnt vmcnt(N) immediate (vmcnt is split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 0xF) | (((n >> 4) & 0x3) << 14); }
+
+// s_waitcnt vmcnt(n) for n = STEP * k, k < kDecTiles, chosen at run time.
+template <int STEP>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (n / STEP) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(1 * STEP)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * STEP)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * STEP)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * STEP)); break;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
+  __shared__ LdsDec<D> lds;
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunks;
+  constexpr int kInstPerTile = 2 * (kBN / kRowsPerInst);  // K and V, 1 KB each
+  constexpr int kInstPerWaveTile = kInstPerTile / 8;      // 4 (D=128) or 2 (D=64)
+  static_assert(kInstPerWaveTile * (kDecTiles - 1) < 64 && kDecTiles <= 5, "vmcnt range");
   const int ngroups = a.hq / a.hpw;
   const int tok = kRows * (4 / a.hpw);
   const int ntok = (a.q_len + tok - 1) / tok;
   const int w = blockIdx.x;
-  const int hg = w % ngroups;
+  const int hg = w % ngroups;  // one KV head per XCD when there are 8 groups
   const int rest = w / ngroups;
   const int tile = rest % ntok;
   const int split = rest / ntok;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int head = hg * a.hpw + wave % a.hpw;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // key half of every tile
+  const int wv = wave & 3;    // wave within its group
+  const int head = hg * a.hpw + wv % a.hpw;
   const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
-  const int kbeg = split * a.chunk;
-  const int kend = min(a.kv_len, kbeg + a.chunk);
+  // key tiles are dealt to the splits as evenly as they go
+  const int ntiles_kv = (a.kv_len + kBN - 1) / kBN;
+  const int t_first = (int)((long long)split * ntiles_kv / a.nsplit);
+  const int t_end = (int)((long long)(split + 1) * ntiles_kv / a.nsplit);
+  const int kbeg = t_first * kBN;
+  const int kend = min(a.kv_len, t_end * kBN);
+  const int ntile_all = t_end - t_first;
 
-  WgPlan p;
-  p.q = a.q + (size_t)head * D;
-  p.k = a.k + (size_t)kv_head * D;
-  p.v = a.v + (size_t)kv_head * D;
-  p.q_rows = a.q_len;
-  p.r1s = kbeg;
-  p.r1e = kend;
-  p.r2s = p.r2e = 0;
-  p.P = kend;  // every query row admits every key below the chunk end
-  p.L = kend;
-  p.B = 0x40000000;
-  p.qw0 = tile * tok + (wave / a.hpw) * kRows;
+  const int kv_elems = a.hkv * D;
+  const uint16_t* kb = a.k + (size_t)kv_head * D;
+  const uint16_t* vb = a.v + (size_t)kv_head * D;
 
+  // Query fragments first, so that every later vmcnt wait covers them.
+  const int qw0 = tile * tok + (wv / a.hpw) * kRows;
+  const int qi = qw0 + (lane & 31);
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 raw = u32x4{0, 0, 0, 0};
+    if (qi < a.q_len) {
+      raw = *reinterpret_cast<const u32x4*>(a.q + ((size_t)qi * a.hq + head) * D + kk * 16 +
+                                            half * 8);
+    }
+    qf[kk] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  // This wave's loads of one tile: instructions wave + 8 j of the tile's
+  // kInstPerTile (K blocks, then V blocks).
+  auto load_tile = [&](int t_round, int t_abs) {
+    const int k0 = kbeg + t_abs * kBN;
+    const int rows = min(kend - k0, kBN);
+    const uint32_t nbytes = (uint32_t)((rows - 1) * kv_elems * 2 + D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * kv_elems, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * kv_elems, nbytes);
+#pragma unroll
+    for (int j = 0; j < kInstPerWaveTile; ++j) {
+      const int i = wave + 8 * j;
+      const bool is_k = i < kInstPerTile / 2;
+      const int row0 = (is_k ? i : i - kInstPerTile / 2) * kRowsPerInst;
+      const int R = row0 + lane / kChunks;
+      const uint32_t voff = (uint32_t)(R * kv_elems * 2 + (((lane % kChunks) ^ swz<D>(R)) * 16));
+      if (is_k) buffer_load_lds16(rk, lds.k[t_round] + row0 * D, voff);
+      else buffer_load_lds16(rv, lds.v[t_round] + row0 * D, voff);
+    }
+  };
+
+  // Per-lane LDS offsets.  K rows of this group's key half (32 rows starting at
+  // 32 grp), V rows of that half through the transposed read.
+  uint32_t koff[D / 16];
+  {
+    const int sw = swz<D>(lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      koff[kk] = (uint32_t)((32 * grp + (lane & 31)) * D * 2 + (((2 * kk + half) ^ sw) * 16));
+  }
+  uint32_t voff[D / 32][2];
+  {
+    const int aa = lane & 15, r = aa >> 2, q = aa & 3, g2 = (lane >> 4) & 1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int row = 32 * grp + 8 * sub + 4 * half + r;
+        const int chunk = 4 * dt + 2 * g2 + (q >> 1);
+        voff[dt][sub] = (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
+      }
+    }
+  }
   WaveState<D> ws;
-  attend<D>(p, a.hq * D, a.hkv * D, a.scale_log2, lds, ws);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
+  ws.m = kNegBig;
+  ws.l = 0.f;
 
-  const int lane = threadIdx.x & 63;
-  const int qi = p.qw0 + (lane & 31);
+  for (int r0 = 0; r0 < ntile_all; r0 += kDecTiles) {
+    const int nt = min(kDecTiles, ntile_all - r0);
+    if (r0 > 0) __syncthreads();  // the previous round's tiles have been consumed
+    for (int t = 0; t < nt; ++t) load_tile(t, r0 + t);
+    for (int t = 0; t < nt; ++t) {
+      // tile t has landed once at most the loads of tiles t+1.. are outstanding
+      wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
+      __syncthreads();
+      const int k0 = kbeg + (r0 + t) * kBN + 32 * grp;  // first key of this group's half
+      const char* kt = reinterpret_cast<const char*>(lds.k[t]);
+      // two independent accumulator chains (even / odd head-dim chunks)
+      f32x16 s = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; kk += 2) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + koff[kk]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + koff[kk + 1]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk + 1], s1, 0, 0, 0);
+      }
+      s += s1;
+      if (k0 + 32 > kend) {  // keys past the chunk's end (zero-filled) are masked
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          s[r] = j < kend ? s[r] : kNegInf;
+        }
+      }
+      float mt[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mt[r / 2] = fmaxf(s[r], s[r + 1]);
+#pragma unroll
+      for (int ww = 4; ww >= 1; ww >>= 1) {
+#pragma unroll
+        for (int i = 0; i < ww; ++i) mt[i] = fmaxf(mt[i], mt[i + ww]);
+      }
+      const float mloc = xhalf_max(mt[0]) * a.scale_log2;
+      const bool grow = mloc > ws.m + kRescaleSlack;
+      const float m_new = grow ? mloc : ws.m;
+      const float alpha = fast_exp2(ws.m - m_new);
+      ws.m = m_new;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha;
+      }
+      const float neg_m = -m_new;
+      float lsum = ws.l * alpha;
+      uint32_t pk[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[r], a.scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(s[r + 1], a.scale_log2, neg_m));
+        lsum += p0 + p1;
+        pk[r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+      ws.l = lsum;
+      const char* vt = reinterpret_cast<const char*>(lds.v[t]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vt + voff[dt][0] + c * 16 * D * 2));
+          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vt + voff[dt][1] + c * 16 * D * 2));
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, ws.acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Merge group B into group A through LDS (the tile buffers are free now).
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(&lds.k[0][0]);  // [4 waves][D/32 * 16 * 64 + 128]
+  constexpr int kWaveFloats = (D / 32) * 16 * 64 + 128;
+  if (grp == 1) {
+    float* dst = mrg + wv * kWaveFloats;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(dt * 16 + r) * 64 + lane] = ws.acc[dt][r];
+    }
+    dst[(D / 32) * 16 * 64 + lane] = ws.m;
+    dst[(D / 32) * 16 * 64 + 64 + lane] = ws.l;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float* src = mrg + wv * kWaveFloats;
+    const float mb = src[(D / 32) * 16 * 64 + lane];
+    const float lb = src[(D / 32) * 16 * 64 + 64 + lane];
+    const float m_new = fmaxf(ws.m, mb);
+    const float sa = fast_exp2(ws.m - m_new), sb = fast_exp2(mb - m_new);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ws.acc[dt][r] = ws.acc[dt][r] * sa + src[(dt * 16 + r) * 64 + lane] * sb;
+    }
+    ws.l = ws.l * sa + lb * sb;
+    ws.m = m_new;
+  }
   const bool valid = qi < a.q_len;
   if (a.nsplit == 1) {
     write_rows<D, false>(ws, valid, a.o + ((size_t)qi * a.hq + head) * D,
                          a.lse + (size_t)head * a.q_len + qi);
-  } else {
-    write_rows<D, true>(ws, valid, a.part_o + (((size_t)split * a.q_len + qi) * a.hq + head) * D,
-                        a.part_lse + ((size_t)split * a.hq + head) * a.q_len + qi);
+    return;
+  }
+  // Partial of this (split, head, 32-token tile), normalised, in the
+  // accumulator's own layout: float4 (dt, g, lane) holds dims
+  // 32 dt + 8 g + 4 (lane / 32) + 0..3 of token lane % 32.  Every store
+  // instruction writes 1 KB contiguous.
+  if (qw0 >= a.q_len) return;  // a wave past the block's last query has no partial
+  const float l = xhalf_sum(ws.l);
+  const float inv = 1.f / l;
+  const int ntok32 = (a.q_len + kRows - 1) / kRows;
+  const size_t ptile = ((size_t)split * a.hq + head) * ntok32 + qw0 / kRows;
+  f32x4* po = reinterpret_cast<f32x4*>(a.part_o + ptile * (size_t)(kRows * D));
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      po[(dt * 4 + gq) * 64 + lane] = f32x4{ws.acc[dt][4 * gq] * inv, ws.acc[dt][4 * gq + 1] * inv,
+                                            ws.acc[dt][4 * gq + 2] * inv, ws.acc[dt][4 * gq + 3] * inv};
+    }
+  }
+  if (half == 0) {
+    a.part_lse[ptile * kRows + (lane & 31)] = (ws.m + fast_log2(l)) * kLn2;
   }
 }
 
-// Merge the split partials of one (query row, head) per wave:
-// lse = log sum_c exp(lse_c);  O = sum_c exp(lse_c - lse) O_c.
+// Merge the split partials: one wave per (head, 32-token tile, 1 KB slice of
+// the partial), so that the merge runs on many compute units at once.  Lane l
+// serves token l % 32; lse = log sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c.
+constexpr int kCombineMaxSplits = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // row = qi * hq + head
-  if (row >= a.q_len * a.hq) return;
-  const int qi = row / a.hq, head = row % a.hq;
-  float mx = kNegInf;
-  for (int c = lane; c < a.nsplit; c += 64) {
-    mx = fmaxf(mx, a.part_lse[((size_t)c * a.hq + head) * a.q_len + qi]);
-  }
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float wts[kCombineMaxSplits][32];  // log2-domain lse, then exp weights
+  constexpr int kSlices = D / 8;                // 1 KB slices of a 32 x D fp32 partial
+  const int ntok32 = (a.q_len + 31) / 32;
+  const int slice = blockIdx.x % kSlices;
+  const int rest = blockIdx.x / kSlices;
+  const int tile = rest % ntok32;
+  const int head = rest / ntok32;
+  const int lane = threadIdx.x;
+  const int row = lane & 31;
+  const size_t tile_stride = (size_t)a.hq * ntok32;  // partial tiles per split
+  const size_t my_tile = (size_t)head * ntok32 + tile;
+  const float* lse_src = a.part_lse + my_tile * 32 + row;
+  float m = kNegBig;
+  int c = 0;
+  for (; c + 8 <= a.nsplit; c += 8) {
+    float x[8];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int u = 0; u < 8; ++u) x[u] = lse_src[(size_t)(c + u) * tile_stride * 32] * kLog2e;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m = fmaxf(m, x[u]);
+      if (lane < 32) wts[c + u][row] = x[u];
+    }
+  }
+  for (; c < a.nsplit; ++c) {
+    const float x = lse_src[(size_t)c * tile_stride * 32] * kLog2e;
+    m = fmaxf(m, x);
+    if (lane < 32) wts[c][row] = x;
+  }
+  __syncthreads();
   float sum = 0.f;
-  for (int c = lane; c < a.nsplit; c += 64) {
-    sum += fast_exp2((a.part_lse[((size_t)c * a.hq + head) * a.q_len + qi] - mx) * kLog2e);
+  for (int cc = 0; cc < a.nsplit; ++cc) {
+    const float wv = fast_exp2(wts[cc][row] - m);
+    sum += wv;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 32) wts[cc][row] = wv;
   }
+  __syncthreads();
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + my_tile * (size_t)(32 * D)) +
+                     slice * 64 + lane;
+  const size_t split_stride = tile_stride * (size_t)(32 * D / 4);  // float4s
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  c = 0;
+  for (; c + 8 <= a.nsplit; c += 8) {
+    f32x4 x[8];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-  const float lse = mx + fast_log2(sum) * kLn2;
-  constexpr int kPer = D / 64;  // dims per lane
-  float acc[kPer];
+    for (int u = 0; u < 8; ++u) x[u] = src[(size_t)(c + u) * split_stride];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  for (int c = 0; c < a.nsplit; ++c) {
-    const float wgt = fast_exp2((a.part_lse[((size_t)c * a.hq + head) * a.q_len + qi] - lse) *
-                                kLog2e);
-    const float* src = a.part_o + (((size_t)c * a.q_len + qi) * a.hq + head) * D + lane * kPer;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] += wgt * src[e];
+    for (int u = 0; u < 8; ++u) acc += wts[c + u][row] * x[u];
   }
-  uint16_t* dst = a.o + ((size_t)qi * a.hq + head) * D + lane * kPer;
-  if constexpr (kPer == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0], acc[1]);
-  } else {
-    dst[0] = static_cast<uint16_t>(pack_bf16x2(acc[0], 0.f) & 0xffffu);
+  for (; c < a.nsplit; ++c) acc += wts[c][row] * src[(size_t)c * split_stride];
+  acc *= 1.f / sum;
+  // slice = dt * 4 + g: dims 32 dt + 8 g + 4 (lane / 32) + 0..3 of token row
+  const int qi = tile * 32 + row;
+  if (qi < a.q_len) {
+    const int d = (slice >> 2) * 32 + (slice & 3) * 8 + 4 * (lane >> 5);
+    *reinterpret_cast<u32x2*>(a.o + ((size_t)qi * a.hq + head) * D + d) =
+        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    if (slice == 0 && lane < 32) a.lse[(size_t)head * a.q_len + qi] = (m + fast_log2(sum)) * kLn2;
   }
-  if (lane == 0) a.lse[(size_t)head * a.q_len + qi] = lse;
 }
 
 }  // namespace
@@ -766,17 +1014,17 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const long long nwg = (long long)ngroups * ntok * a.nsplit;
   if (nwg <= 0) return hipSuccess;
   if (a.d == 128) {
-    hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)nwg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)nwg), dim3(kPPThreads), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nsplit == 1) return err;
-  const unsigned nrows = (unsigned)a.q_len * a.hq;
+  const unsigned ncomb = (unsigned)((a.q_len + 31) / 32) * a.hq * (a.d / 8);
   if (a.d == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((nrows + 3) / 4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(ncomb), dim3(64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((nrows + 3) / 4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(ncomb), dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -31,7 +31,7 @@ bca_status_t hip_status(hipError_t err, const char* what) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxDecodeSplits = 1024;
+constexpr int kMaxDecodeSplits = 256;  // the combine kernel stages one weight per split and row
 
 // Checks shared by the packed-segment entry points.
 bca_status_t check_packed(const void* q, const void* k, const void* v, const void* o,
@@ -184,22 +184,28 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
                     "backward launch");
 }
 
-// Split-KV plan of the decode step: key chunks are whole 64-key tiles, and
-// the count aims at roughly two workgroups per compute unit of the 256-CU part.
-static int decode_splits(int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t req,
-                         int* chunk_out) {
+// Split-KV plan of the decode step: the 64-key tiles are dealt evenly to
+// the splits.  By default a split is one round of at most the 5 tiles a
+// workgroup stages in LDS, with at least 8 splits of 2 or more tiles for a
+// short cache, and no more workgroups than the 256 compute units while that
+// allows (a longer split is processed in rounds).
+static int decode_splits(int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t req) {
   const int hpw = bca::heads_per_wg(hq, hkv);
   const int tok = 32 * (4 / hpw);
   const int ntok = (q_len + tok - 1) / tok;
   const int base_wgs = (hq / hpw) * ntok;
   const int tiles = (kv_len + 63) / 64;
-  int want = req > 0 ? req : (256 + base_wgs - 1) / base_wgs;
-  if (want > tiles) want = tiles;
-  if (want > kMaxDecodeSplits) want = kMaxDecodeSplits;
-  if (want < 1) want = 1;
-  const int tiles_per = (tiles + want - 1) / want;
-  *chunk_out = tiles_per * 64;
-  return (kv_len + *chunk_out - 1) / *chunk_out;
+  int ns;
+  if (req > 0) {
+    ns = req;
+  } else {
+    ns = (tiles + 4) / 5;
+    if (ns < 8) ns = tiles / 2 < 8 ? tiles / 2 : 8;
+    const int cap = base_wgs < 256 ? 256 / base_wgs : 1;
+    if (ns > cap) ns = cap;
+  }
+  if (ns > tiles) ns = tiles;
+  return ns < 1 ? 1 : ns;
 }
 
 size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
@@ -207,11 +213,11 @@ size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t h
   if (q_len <= 0 || kv_len <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || (d != 64 && d != 128) ||
       num_splits < 0)
     return 0;
-  int chunk;
-  const int ns = decode_splits(q_len, kv_len, hq, hkv, num_splits, &chunk);
+  const int ns = decode_splits(q_len, kv_len, hq, hkv, num_splits);
   if (ns <= 1) return 0;
-  const size_t po = ((size_t)ns * q_len * hq * d * sizeof(float) + 255) & ~(size_t)255;
-  const size_t pl = ((size_t)ns * hq * q_len * sizeof(float) + 255) & ~(size_t)255;
+  const size_t rows = (size_t)ns * hq * ((q_len + 31) / 32) * 32;
+  const size_t po = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+  const size_t pl = (rows * sizeof(float) + 255) & ~(size_t)255;
   return po + pl;
 }
 
@@ -232,8 +238,7 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   if (!q || !k || !v || !o || !lse) return fail(BCA_ERR_NULL, "a required pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BCA_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
-  int chunk;
-  const int ns = decode_splits(q_len, kv_len, hq, hkv, num_splits, &chunk);
+  const int ns = decode_splits(q_len, kv_len, hq, hkv, num_splits);
   const size_t need = bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -244,7 +249,8 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   a.v = static_cast<const uint16_t*>(v);
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
-  const size_t po = ((size_t)ns * q_len * hq * d * sizeof(float) + 255) & ~(size_t)255;
+  const size_t po =
+      ((size_t)ns * hq * ((q_len + 31) / 32) * 32 * d * sizeof(float) + 255) & ~(size_t)255;
   a.part_o = ns > 1 ? static_cast<float*>(workspace) : nullptr;
   a.part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
   a.q_len = q_len;
@@ -253,7 +259,6 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   a.hkv = hkv;
   a.d = d;
   a.hpw = bca::heads_per_wg(hq, hkv);
-  a.chunk = chunk;
   a.nsplit = ns;
   a.scale_log2 = scale * kLog2e;
   return hip_status(bca::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode launch");

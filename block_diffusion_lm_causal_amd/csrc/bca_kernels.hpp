@@ -39,11 +39,13 @@ struct DecodeArgs {
   const uint16_t* v;
   uint16_t* o;        // [q_len, hq, d]
   float* lse;         // [hq, q_len]
-  float* part_o;      // [nsplit, q_len, hq, d] (nsplit > 1)
-  float* part_lse;    // [nsplit, hq, q_len]
+  // Split partials (nsplit > 1), per (split, head, 32-token tile):
+  // part_o   [nsplit, hq, ceil(q_len/32), 32 * d] in the MFMA accumulator order
+  // part_lse [nsplit, hq, ceil(q_len/32), 32]
+  float* part_o;
+  float* part_lse;
   int q_len, kv_len, hq, hkv, d, hpw;
-  int chunk;          // keys per split (multiple of 64)
-  int nsplit;
+  int nsplit;         // split s takes key tiles [s T / nsplit, (s + 1) T / nsplit), T = ceil(kv_len / 64)
   float scale_log2;
 };
 

@@ -154,7 +154,8 @@ size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t h
  *   o          : output [q_len, hq, d] bf16
  *   lse        : output [hq, q_len] float32
  *   num_splits : number of key chunks processed in parallel (split-KV) and
- *                merged by log-sum-exp weights; 0 = chosen by the library
+ *                merged by log-sum-exp weights, in [0, 256]; 0 = chosen by
+ *                the library; a count above ceil(kv_len / 64) is lowered to it
  *   workspace  : device buffer of at least
  *                bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
  *                bytes (may be NULL when that size is 0); contents undefined

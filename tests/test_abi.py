@@ -124,6 +124,7 @@ def test_decode_workspace_and_checks(L):
     assert dec(L, FAKE, need, d=32) == UNSUP
     assert dec(L, FAKE, need, dt=F32) == DTYPE
     assert dec(L, FAKE, need, ns=-2) == SHAPE
+    assert dec(L, FAKE, need, ns=257) == SHAPE
     assert dec(L, FAKE, need, q=None) == NULL
 
 
