@@ -22,6 +22,7 @@ under ``"paths"``:
 headline workload (whole query heads until about 10 s have elapsed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
+       [--only-headline] [--paths decode,staircase] [--copy-calibration]
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -234,6 +235,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline case only")
+    ap.add_argument("--paths", default="decode,staircase",
+                    help="comma list of extra paths to time: decode, staircase (or none)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (a known-size "
+                         "kernel against which HBM byte counters are scaled)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -246,6 +252,17 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_launch": nbytes,
+                                               "bytes_written_per_launch": nbytes,
+                                               "launches": 5}}), flush=True)
+        return 0
     from block_diffusion_lm_causal_amd import bca, workloads
     bca.lib()  # fails loudly if the HIP library is missing
 
@@ -258,10 +275,12 @@ def main() -> int:
     traffic = stored_traffic("fwd_bf16_prefill_L4096")
 
     paths = {}
-    if not args.only_headline:
+    extra = set() if args.only_headline else set(p for p in args.paths.split(",") if p)
+    if "decode" in extra:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")
             paths[f"decode_P{P}"] = bench_decode(P)
+    if "staircase" in extra:
         log("[bench] staircase forward, 8 trajectories")
         paths["staircase_fwd_8traj"] = bench_staircase(workloads.staircase_fwd_8traj,
                                                        max(5, args.steps // 5), 3, False)
@@ -288,7 +307,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "seq_len": 4096, "block_size": 32, "hq": 32, "hkv": 8,
-                   "head_dim": 128, "batch": 1, "kernel": "fwd_bf16_kernel<128>",
+                   "head_dim": 128, "batch": 1, "kernel": "fwd_pp_kernel<128>",
                    "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

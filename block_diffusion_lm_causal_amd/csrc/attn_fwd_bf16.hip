@@ -8,15 +8,15 @@
 // prefix KV cache (thread page, Result 4).  The admitted-key rule is in
 // bca_device.hpp.
 //
-// Work decomposition.  A workgroup is 4 wave64s.  Each wave owns 32 query rows
-// of one query head; the workgroup's waves are `hpw` query heads that share a
-// KV head (GQA) times 4/hpw consecutive 32-row sub-tiles, so K/V tiles staged
-// in LDS serve all of them.  The workgroup walks only the key tiles its rows
-// admit (whole masked tiles are never issued), 64 keys at a time.
+// Work decomposition.  A forward workgroup is 8 wave64s.  Each wave owns 32
+// query rows of one query head; the waves are `hpw` query heads that share a
+// KV head (GQA) times 8/hpw consecutive 32-row sub-tiles, so K/V tiles
+// staged in LDS serve all of them.  The workgroup walks only the key tiles its rows admit (whole masked
+// tiles are never issued), 64 keys at a time.
 //
 // Data movement.  K and V tiles go from HBM straight into LDS
 // (buffer_load ... lds, 16 bytes per lane), double-buffered, with the next
-// tile in flight while the current one is multiplied.  The buffer resource of
+// tiles in flight while the current one is multiplied.  The buffer resource of
 // each tile ends at the tile's last valid key, so rows past it arrive as zeros
 // without any per-lane work.  Tiles are stored row-major with a 16-byte chunk
 // swizzle (bca_device.hpp) that keeps both LDS read patterns conflict-free.
@@ -38,55 +38,9 @@
 namespace bca {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBN = 64;    // keys per tile
 constexpr int kRows = 32;  // query rows per wave
 constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before rescaling
-
-// K tiles are double-buffered; V tiles triple-buffered because P V of a tile
-// runs one iteration after its Q K^T (see attend()).
-template <int D>
-struct Lds {
-  uint16_t k[2][kBN * D];
-  uint16_t v[3][kBN * D];
-};
-
-// Direct HBM -> LDS loads of one K and one V tile.
-template <int D>
-struct TileLoader {
-  static constexpr int kChunks = D / 8;                      // 16-byte chunks per row
-  static constexpr int kRowsPerInst = 64 / kChunks;          // rows one instruction fills
-  static constexpr int kInstPerWave = kBN / kRowsPerInst / 4;
-  uint32_t voff[kInstPerWave];  // per-lane byte offset inside the tile
-  int lds_row0[kInstPerWave];   // first row written by each instruction (wave-uniform)
-
-  __device__ __forceinline__ void init(int row_bytes, int tid) {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-#pragma unroll
-    for (int i = 0; i < kInstPerWave; ++i) {
-      const int row0 = (i * 4 + wave) * kRowsPerInst;
-      const int R = row0 + lane / kChunks;
-      const int c = (lane % kChunks) ^ swz<D>(R);  // logical chunk landing in this lane's slot
-      voff[i] = (uint32_t)(R * row_bytes + c * 16);
-      lds_row0[i] = row0;
-    }
-  }
-
-  // keys [k0, min(k0 + 64, kend)) of rows with byte stride row_bytes
-  __device__ __forceinline__ void issue(const uint16_t* kb, const uint16_t* vb, int row_elems,
-                                        int k0, int kend, Lds<D>& lds, int kbuf, int vbuf) {
-    // only rows [0, 64) of the tile are ever read, so the range never needs more
-    const int rows = min(kend - k0, kBN);
-    const uint32_t nbytes = (uint32_t)((rows - 1) * row_elems * 2 + D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * row_elems, nbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_elems, nbytes);
-#pragma unroll
-    for (int i = 0; i < kInstPerWave; ++i) {
-      buffer_load_lds16(rk, &lds.k[kbuf][lds_row0[i] * D], voff[i]);
-      buffer_load_lds16(rv, &lds.v[vbuf][lds_row0[i] * D], voff[i]);
-    }
-  }
-};
 
 // Everything a workgroup needs to know about its rows and keys.
 struct WgPlan {
@@ -123,203 +77,6 @@ __device__ __forceinline__ void pv_update(const char* vt, const uint32_t (&voff)
       ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, ws.acc[dt], 0, 0, 0);
     }
   }
-}
-
-// The tile loop: accumulates softmax(scale * q K^T) V over the planned key
-// ranges into ws (unnormalised, with running max and partial sums).
-template <int D>
-__device__ __forceinline__ void attend(const WgPlan& p, int q_stride, int kv_stride,
-                                       float scale_log2, Lds<D>& lds, WaveState<D>& ws) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int qi = p.qw0 + (lane & 31);
-  const bool wave_active = p.qw0 < p.q_rows;
-  const int qw_last = min(p.qw0 + kRows, p.q_rows) - 1;
-
-  TileLoader<D> ld;
-  ld.init(kv_stride * 2, tid);
-  const int n1 = (p.r1e - p.r1s + kBN - 1) / kBN;
-  const int n2 = p.r2e > p.r2s ? (p.r2e - p.r2s + kBN - 1) / kBN : 0;
-  const int ntile = n1 + n2;
-  if (ntile > 0) ld.issue(p.k, p.v, kv_stride, p.r1s, p.r1e, lds, 0, 0);
-
-  // Query fragments: B operand of S^T = K Q^T, 8 consecutive dims per lane.
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 raw = u32x4{0, 0, 0, 0};
-    if (qi < p.q_rows) {
-      raw = *reinterpret_cast<const u32x4*>(p.q + (size_t)qi * q_stride + kk * 16 + half * 8);
-    }
-    qf[kk] = __builtin_bit_cast(bf16x8, raw);
-  }
-
-  const RowKeys rk = row_keys(qi < p.q_rows ? qi : qw_last, p.P, p.L, p.B);
-  const RowKeys rkA = row_keys(p.qw0 < p.q_rows ? p.qw0 : 0, p.P, p.L, p.B);
-  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, p.P, p.L, p.B);
-  const int first_copy_row = p.qw0 > p.P ? p.qw0 : p.P;
-  const int s2_first = (qw_last >= p.P) ? row_keys(first_copy_row, p.P, p.L, p.B).s2 : 0x7fffffff;
-  const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
-
-  // Per-lane LDS byte offsets inside a tile.
-  // K (A operand of S^T): row lane%32 (+32 for the second key half), logical chunk 2kk + half.
-  uint32_t koff[D / 16];
-  {
-    const int s = swz<D>(lane & 15);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      koff[kk] = (uint32_t)((lane & 31) * D * 2 + (((2 * kk + half) ^ s) * 16));
-  }
-  // V (A operand of O^T, transposed read): 16-lane group G, address-lane 4r + q reads
-  // rows 16c + 8sub + 4half + r, dims 32dt + 16(G%2) + 4q.
-  uint32_t voff[D / 32][2];
-  {
-    const int a = lane & 15, r = a >> 2, q = a & 3, g2 = (lane >> 4) & 1;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int row = 8 * sub + 4 * half + r;
-        const int chunk = 4 * dt + 2 * g2 + (q >> 1);
-        voff[dt][sub] = (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
-  ws.m = kNegBig;
-  ws.l = 0.f;
-  if (ntile == 0) return;
-  {
-    // V buffer 2 stands in for "the tile before the first one": zeros.
-    u32x4* z = reinterpret_cast<u32x4*>(lds.v[2]);
-#pragma unroll
-    for (int i = 0; i < kBN * D * 2 / 16 / kThreads; ++i) z[tid + i * kThreads] = u32x4{0, 0, 0, 0};
-  }
-
-  wait_vmem();
-  __syncthreads();
-
-  // Software pipeline.  Iteration t computes S^T and the softmax of tile t and,
-  // interleaved with those exponentials, O^T += V^T P^T of tile t-1 (independent
-  // work, so MFMA and VALU overlap inside the wave).  Tile t+1 is put in flight
-  // at the top of the iteration.  A rescale of O (rare) is applied after the
-  // P V of tile t-1 has been accumulated against the old maximum.  Tile t uses V
-  // buffer t % 3; before the first tile the "previous" buffer (2) holds zeros
-  // and P is zero, so the loop body needs no first-iteration branch.  A wave
-  // whose rows admit no key of a tile runs it fully masked (P = 0).
-  uint32_t pk[kBN / 16][4];  // P^T of the previous tile, bf16 pairs
-#pragma unroll
-  for (int c = 0; c < kBN / 16; ++c) pk[c][0] = pk[c][1] = pk[c][2] = pk[c][3] = 0u;
-  int vbuf_prev = 2, vbuf = 0;
-  float alpha_prev = 1.f;     // rescale decided by the previous tile, not yet applied to O
-  bool rescale_prev = false;  // wave-uniform
-  for (int t = 0; t < ntile; ++t) {
-    // O must be rescaled after the P V of tile t-2 (done last iteration) and
-    // before that of tile t-1 (done below).
-    if (rescale_prev) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
-    }
-    const int kbuf = t & 1;
-    const int vbuf_next = vbuf == 2 ? 0 : vbuf + 1;
-    if (t + 1 < ntile) {
-      const int t1 = t + 1;
-      ld.issue(p.k, p.v, kv_stride, t1 < n1 ? p.r1s + t1 * kBN : p.r2s + (t1 - n1) * kBN,
-               t1 < n1 ? p.r1e : p.r2e, lds, kbuf ^ 1, vbuf_next);
-    }
-    const char* vprev = reinterpret_cast<const char*>(lds.v[vbuf_prev]);
-    const int k0 = t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN;
-    const int kend = t < n1 ? p.r1e : p.r2e;
-    const bool full = wave_active && (k0 + kBN <= kend) &&
-                      ((k0 + kBN <= rkA.e1) ||
-                       (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
-    const char* kt = reinterpret_cast<const char*>(lds.k[kbuf]);
-    // S^T tile: two 32-key halves.
-    f32x16 s[kBN / 32];
-#pragma unroll
-    for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
-      }
-    }
-    // Mask (partial tiles only).
-    if (!full) {
-#pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
-          s[h][r] = ok ? s[h][r] : kNegInf;
-        }
-      }
-    }
-    // Row max, softmax of tile t, interleaved with P V of tile t-1.
-    // tree reduction (short dependency chain), then the other half-wave
-    float mt[kBN / 4];
-#pragma unroll
-    for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
-    }
-#pragma unroll
-    for (int w = kBN / 8; w >= 1; w >>= 1) {
-#pragma unroll
-      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
-    }
-    const float mloc = xhalf_max(mt[0]) * scale_log2;
-    // Move a row's running max only when the row outgrew it by the slack (a
-    // per-lane select: no branch splits the softmax from the P V MFMAs below).
-    const bool grow = mloc > ws.m + kRescaleSlack;
-    const float m_new = grow ? mloc : ws.m;
-    const float alpha = fast_exp2(ws.m - m_new);
-    ws.m = m_new;
-    const float neg_m = -m_new;
-    float lsum = ws.l * alpha;
-    uint32_t pn[kBN / 16][4];
-#pragma unroll
-    for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
-        const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
-        lsum += p0 + p1;  // float32 sum of the unrounded probabilities
-        pn[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
-    }
-    ws.l = lsum;
-    pv_update<D>(vprev, voff, pk, ws);
-    // Issue order hint: two transposed V reads, one MFMA, then softmax VALU work.
-#pragma unroll
-    for (int i = 0; i < (kBN / 16) * (D / 32); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
-    rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
-    alpha_prev = alpha;
-#pragma unroll
-    for (int c = 0; c < kBN / 16; ++c) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[c][e] = pn[c][e];
-    }
-    vbuf_prev = vbuf;
-    vbuf = vbuf_next;
-    wait_vmem();
-    __syncthreads();
-  }
-  if (rescale_prev) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
-  }
-  pv_update<D>(reinterpret_cast<const char*>(lds.v[vbuf_prev]), voff, pk, ws);
 }
 
 // Write the normalised rows of a wave: O as bf16 (or float32 partials) and LSE.
@@ -597,56 +354,6 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a, int nt
 
   WaveState<D> ws;
   attend_pp<D>(p, a.hq * D, a.hkv * D, a.scale_log2, lds, ws);
-
-  const int lane = threadIdx.x & 63;
-  const int qi = p.qw0 + (lane & 31);
-  write_rows<D, false>(ws, qi < L, a.o + ((size_t)(base + qi) * a.hq + head) * D,
-                       a.lse + (size_t)head * a.total + base + qi);
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
-  __shared__ Lds<D> lds;
-  const int ngroups = a.hq / a.hpw;
-  const int tok = kRows * (4 / a.hpw);
-  const int w = blockIdx.x;
-  const int hg = w % ngroups;
-  const int rest = w / ngroups;
-  const int seg = rest % a.nseq;
-  const int rank = rest / a.nseq;
-
-  const int base = a.cu_seqlens[seg];
-  const int L = a.cu_seqlens[seg + 1] - base;
-  const int ntiles = (L + tok - 1) / tok;
-  if (rank >= ntiles) return;
-  const int tile = ntiles - 1 - rank;  // costliest (last) tiles of every segment first
-  const int S = a.s_copies ? a.s_copies[seg] : 0;
-  int P = L - S * a.block_size;
-  if (P < 0) P = 0;
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int head = hg * a.hpw + wave % a.hpw;
-  const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
-  const int q0 = tile * tok;
-  const int q_last = min(q0 + tok, L) - 1;
-  const TileKeys tk = tile_keys(q0, q_last, P, L, a.block_size);
-
-  WgPlan p;
-  p.q = a.q + (size_t)base * a.hq * D + (size_t)head * D;
-  p.k = a.k + (size_t)base * a.hkv * D + (size_t)kv_head * D;
-  p.v = a.v + (size_t)base * a.hkv * D + (size_t)kv_head * D;
-  p.q_rows = L;
-  p.r1s = 0;
-  p.r1e = tk.r1e;
-  p.r2s = tk.r2s;
-  p.r2e = tk.r2e;
-  p.P = P;
-  p.L = L;
-  p.B = a.block_size;
-  p.qw0 = q0 + (wave / a.hpw) * kRows;
-
-  WaveState<D> ws;
-  attend<D>(p, a.hq * D, a.hkv * D, a.scale_log2, lds, ws);
 
   const int lane = threadIdx.x & 63;
   const int qi = p.qw0 + (lane & 31);
