@@ -24,7 +24,7 @@
 //      their B operands (dO and Q with queries on K) come from the row-major
 //      tiles through the transposed LDS read.
 //   3. dQ: shaped like the forward's ping-pong kernel -- two groups of four
-//      waves, one phase apart, over 64-key tiles: MFMA phase S^T(t) = K Q^T,
+//      waves, one phase apart, over 32-key tiles: MFMA phase S^T(t) = K Q^T,
 //      dP^T(t) = V dO^T and dQ^T += K^T dS^T(t-1); VALU phase P and dS of
 //      tile t.  K^T comes from the row-major K tile through the transposed read.
 #include "bca_device.hpp"
