@@ -111,13 +111,33 @@ __device__ __forceinline__ void write_rows(const WaveState<D>& ws, bool valid, v
 // one wave of each group per SIMD).  Both groups consume the same K/V tiles;
 // B runs one phase behind A, so on every SIMD one wave is in an MFMA phase
 // (S^T of tile t and O^T += V^T P^T of tile t-1) while the other is in its
-// softmax phase (VALU), and they swap at each barrier.  Phase phi:
-//   A: phi even -> MFMA(phi/2), phi odd -> softmax((phi-1)/2)
-//   B: the same with phi - 1.
-// At even phi = 2t every wave issues its share of the loads of K(t+1) and V(t)
-// (double buffers for both), which complete by the end of phase 2t+1.
+// softmax phase (VALU), and they swap at each barrier.  Phases 2t and 2t+1:
+//   A: MFMA(t), then softmax(t);   B: softmax(t-1), then MFMA(t).
+// Each group runs its own straight-line loop (two barriers per iteration, so
+// both groups pass the same barriers), which keeps S and P in fixed registers.
+// Only group A loads K/V: in phase 2t, after its own LDS reads, it issues
+// K(t+1) and V(t) into the buffers last read in phase 2t-1 (double buffers),
+// and waits for them at the end of phase 2t+1.  Group B never has a tile
+// load in flight, so none of its LDS reads waits on one.
 
 constexpr int kPPThreads = 512;
+
+// Workgroup barrier that leaves direct-to-LDS loads in flight.  __syncthreads()
+// would wait for them: its release fence waits for every earlier memory
+// operation.  LDS reads issued before this barrier have returned (lgkmcnt),
+// so a buffer may be overwritten after it; the memory clobber keeps the
+// compiler from moving memory accesses across it.  Data of a direct load is
+// visible to other waves only once its issuer has waited for it (vmcnt) and
+// then passed a barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The same, after this wave's direct-to-LDS loads have landed.  Written as one
+// asm block so that the wait stays at the end of the phase.
+__device__ __forceinline__ void wait_vmem_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int D>
 struct LdsPP {
@@ -125,24 +145,26 @@ struct LdsPP {
   uint16_t v[2][kBN * D];
 };
 
+// Direct HBM -> LDS loads of one 64-key tile, issued by the 4 waves of group A.
 template <int D>
 struct PPLoader {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kRowsPerInst = 64 / kChunks;
-  static constexpr int kInstPerWave = kBN / kRowsPerInst / 8;  // per tensor
+  static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;            // rows one instruction fills
+  static constexpr int kInstPerWave = kBN / kRowsPerInst / 4;  // per tensor
   uint32_t voff[kInstPerWave];
   int lds_row0[kInstPerWave];
 
   __device__ __forceinline__ void init(int row_bytes, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kInstPerWave; ++i) {
-      const int row0 = (i * 8 + wave) * kRowsPerInst;
+      const int row0 = (i * 4 + wave) * kRowsPerInst;
       const int R = row0 + lane / kChunks;
-      const int c = (lane % kChunks) ^ swz<D>(R);
+      const int c = (lane % kChunks) ^ swz<D>(R);  // logical chunk landing in this lane's slot
       voff[i] = (uint32_t)(R * row_bytes + c * 16);
       lds_row0[i] = row0;
     }
   }
+  // keys [k0, min(k0 + 64, kend)); rows past kend arrive as zeros
   __device__ __forceinline__ void issue(const uint16_t* base, int row_elems, int k0, int kend,
                                         uint16_t* dst) {
     const int rows = min(kend - k0, kBN);
@@ -166,13 +188,13 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
   const int qw_last = min(p.qw0 + kRows, p.q_rows) - 1;
 
   PPLoader<D> ld;
-  ld.init(kv_stride * 2, wave, lane);
+  ld.init(kv_stride * 2, wave & 3, lane);
   const int n1 = (p.r1e - p.r1s + kBN - 1) / kBN;
   const int n2 = p.r2e > p.r2s ? (p.r2e - p.r2s + kBN - 1) / kBN : 0;
   const int ntile = n1 + n2;
   auto tile_k0 = [&](int t) { return t < n1 ? p.r1s + t * kBN : p.r2s + (t - n1) * kBN; };
   auto tile_end = [&](int t) { return t < n1 ? p.r1e : p.r2e; };
-  if (ntile > 0) ld.issue(p.k, kv_stride, tile_k0(0), tile_end(0), lds.k[0]);
+  if (ntile > 0 && grp == 0) ld.issue(p.k, kv_stride, tile_k0(0), tile_end(0), lds.k[0]);
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -221,90 +243,139 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
   uint32_t pk[kBN / 16][4];   // P^T of the tile between its softmax and P V phases
   float alpha_prev = 1.f;
   bool rescale_prev = false;
-  const int nphase = 2 * ntile + 2;
-  for (int phi = 0; phi < nphase; ++phi) {
-    if ((phi & 1) == 0) {
-      const int t = phi >> 1;
-      if (t + 1 < ntile) ld.issue(p.k, kv_stride, tile_k0(t + 1), tile_end(t + 1), lds.k[(t + 1) & 1]);
-      if (t < ntile) ld.issue(p.v, kv_stride, tile_k0(t), tile_end(t), lds.v[t & 1]);
+
+  // MFMA phase: the rescale pending from the previous softmax, O^T += V^T P^T
+  // of tile t-1 (t >= 1), then S^T of tile t (t < ntile).
+  auto mfma_phase = [&](int t, bool do_pv, bool do_s) {
+    if (rescale_prev) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
     }
-    const int my = phi - grp;
-    if (my >= 0 && (my & 1) == 0) {
-      // MFMA phase for tile tm: rescale pending from softmax(tm-1), P V of
-      // tile tm-1, then S^T of tile tm.
-      const int tm = my >> 1;
-      if (rescale_prev) {
+    if (do_pv) pv_update<D>(reinterpret_cast<const char*>(lds.v[(t - 1) & 1]), voff, pk, ws);
+    if (do_s) {
+      // K fragments (kk, h) in order i = 2 kk + h, read kAhead ahead of use
+      // so that LDS latency hides behind the MFMAs; the scheduling groups
+      // below pin that order (left alone, the scheduler reads only two ahead).
+      const char* kt = reinterpret_cast<const char*>(lds.k[t & 1]);
+      constexpr int kFrags = (D / 16) * (kBN / 32);
+      constexpr int kAhead = 4;
+      auto frag = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(kt + koff[i / 2] + (i % 2) * 32 * D * 2);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 kb[kAhead];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
+      for (int i = 0; i < kAhead; ++i) kb[i] = frag(i);
+#pragma unroll
+      for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < kFrags; ++i) {
+        s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % kAhead], qf[i / 2], s[i % 2], 0, 0, 0);
+        if (i + kAhead < kFrags) kb[i % kAhead] = frag(i + kAhead);
       }
-      if (tm >= 1) {
-        pv_update<D>(reinterpret_cast<const char*>(lds.v[(tm - 1) & 1]), voff, pk, ws);
+      // issue order: kAhead LDS reads, then (MFMA, read) pairs, then MFMAs
+      // (group masks: 0x100 LDS read, 0x008 MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kFrags - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      if (tm < ntile) {
-        const char* kt = reinterpret_cast<const char*>(lds.k[tm & 1]);
-#pragma unroll
-        for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-          for (int h = 0; h < kBN / 32; ++h) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[kk] + h * 32 * D * 2);
-            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[h], 0, 0, 0);
-          }
-        }
-      }
-    } else if (my >= 0 && (my >> 1) < ntile) {
-      // Softmax phase for tile tv.
-      const int tv = my >> 1;
-      const int k0 = tile_k0(tv), kend = tile_end(tv);
-      const bool full = wave_active && (k0 + kBN <= kend) &&
-                        ((k0 + kBN <= rkA.e1) ||
-                         (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
-      if (!full) {
-#pragma unroll
-        for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
-            s[h][r] = ok ? s[h][r] : kNegInf;
-          }
-        }
-      }
-      float mt[kBN / 4];
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax phase of tile t: mask (only where the tile is not wholly
+  // admitted for this wave), running max with lazy rescale, P in bf16.
+  auto softmax_phase = [&](int t) {
+    const int k0 = tile_k0(t), kend = tile_end(t);
+    const bool full = wave_active && (k0 + kBN <= kend) &&
+                      ((k0 + kBN <= rkA.e1) ||
+                       (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+    if (!full) {
 #pragma unroll
       for (int h = 0; h < kBN / 32; ++h) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
-      }
-#pragma unroll
-      for (int w = kBN / 8; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
-      }
-      const float mloc = xhalf_max(mt[0]) * scale_log2;
-      const bool grow = mloc > ws.m + kRescaleSlack;
-      const float m_new = grow ? mloc : ws.m;
-      const float alpha = fast_exp2(ws.m - m_new);
-      ws.m = m_new;
-      const float neg_m = -m_new;
-      float lsum = ws.l * alpha;
-#pragma unroll
-      for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
-          const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
-          lsum += p0 + p1;
-          pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+          s[h][r] = ok ? s[h][r] : kNegInf;
         }
       }
-      ws.l = lsum;
-      rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
-      alpha_prev = alpha;
     }
-    if (phi & 1) wait_vmem();
-    __syncthreads();
+    float mt[kBN / 4];
+#pragma unroll
+    for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
+    }
+#pragma unroll
+    for (int w = kBN / 8; w >= 1; w >>= 1) {
+#pragma unroll
+      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
+    }
+    const float mloc = xhalf_max(mt[0]) * scale_log2;
+    const bool grow = mloc > ws.m + kRescaleSlack;
+    const float m_new = grow ? mloc : ws.m;
+    const float alpha = fast_exp2(ws.m - m_new);
+    ws.m = m_new;
+    const float neg_m = -m_new;
+    float lsum = ws.l * alpha;
+#pragma unroll
+    for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(fmaf(s[h][r], scale_log2, neg_m));
+        const float p1 = fast_exp2(fmaf(s[h][r + 1], scale_log2, neg_m));
+        lsum += p0 + p1;
+        pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+    }
+    ws.l = lsum;
+    rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
+    alpha_prev = alpha;
+  };
+
+  // Group A's loads in phase 2t: K(t+1) and V(t).
+  auto issue = [&](int t) {
+    if (t + 1 < ntile) ld.issue(p.k, kv_stride, tile_k0(t + 1), tile_end(t + 1), lds.k[(t + 1) & 1]);
+    if (t < ntile) ld.issue(p.v, kv_stride, tile_k0(t), tile_end(t), lds.v[t & 1]);
+  };
+
+  // Phase barriers are barrier_lds(): the loads issued in phase 2t stay in
+  // flight across the barrier that ends it and are waited for (vmcnt) only at
+  // the end of phase 2t+1.
+  if (grp == 0) {
+    mfma_phase(0, false, true);
+    issue(0);
+    barrier_lds();
+    softmax_phase(0);
+    wait_vmem_barrier();
+    for (int t = 1; t < ntile; ++t) {
+      mfma_phase(t, true, true);
+      issue(t);
+      barrier_lds();
+      softmax_phase(t);
+      wait_vmem_barrier();
+    }
+    mfma_phase(ntile, true, false);
+    barrier_lds();
+    barrier_lds();
+  } else {
+    barrier_lds();
+    mfma_phase(0, false, true);
+    barrier_lds();
+    for (int t = 1; t < ntile; ++t) {
+      softmax_phase(t - 1);
+      barrier_lds();
+      mfma_phase(t, true, true);
+      barrier_lds();
+    }
+    softmax_phase(ntile - 1);
+    barrier_lds();
+    mfma_phase(ntile, true, false);
+    barrier_lds();
   }
 }
 
