@@ -13,7 +13,8 @@ under ``"paths"``:
     block's own 32 (GQA 32/8, d 128): HBM GB/s of the algorithmic bytes
     (K and V read once per KV head, Q read, O and LSE written), median over
     32 calls with L2 and the Infinity Cache flushed before each call, plus the
-    warm back-to-back figure, labelled;
+    warm back-to-back figure and the per-step time of a captured 32-step
+    graph (caches warm), labelled;
   * staircase forward, 8 packed trajectories (block 32);
   * staircase forward and backward, 16 packed trajectories (block 64),
     backward FLOPs counted as 10 * d per admitted pair per query head.
@@ -146,6 +147,11 @@ def bench_decode(prefix: int, calls: int = 32):
     warm, _ = timed_calls(step, calls, 3)
     cold_us = statistics.median(cold) * 1e3
     warm_us = statistics.median(warm) * 1e3
+    # the denoising loop of one block as one captured graph of `calls` steps
+    graph = bca.DecodeGraph(q, k, v, calls, w.scale, workspace=ws, out=o, lse=lse)
+    replays, _ = timed_calls(graph.launch, 10, 2)
+    graph.close()
+    graph_us = statistics.median(replays) * 1e3 / calls
     return {
         "workload": w.name, "bytes_per_call": algo_bytes,
         "us_per_call_flushed_median": round(cold_us, 3),
@@ -153,6 +159,8 @@ def bench_decode(prefix: int, calls: int = 32):
         "frac_hbm_flushed": round(algo_bytes / cold_us / 1e3 / PEAK_HBM_GBS, 4),
         "us_per_call_warm_median": round(warm_us, 3),
         "GBps_warm_l2_resident": round(algo_bytes / warm_us / 1e3, 1),
+        "us_per_step_graph_replay": round(graph_us, 3),
+        "GBps_graph_replay_l2_resident": round(algo_bytes / graph_us / 1e3, 1),
         "calls": calls,
     }
 

@@ -25,6 +25,7 @@ BCA_BF16 = 1
 EXPORTS = (
     "bca_abi_version", "bca_status_string", "bca_last_error", "bca_fwd", "bca_staircase_fwd",
     "bca_staircase_bwd_workspace", "bca_staircase_bwd", "bca_decode_workspace", "bca_decode",
+    "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
 )
 
 
@@ -74,6 +75,13 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_workspace.argtypes = [_I, _I, _I, _I, _I, _I]
     L.bca_decode.restype = _I
     L.bca_decode.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]
+    L.bca_decode_graph_create.restype = _I
+    L.bca_decode_graph_create.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P,
+                                          _S, _I, ctypes.POINTER(_P)]
+    L.bca_decode_graph_launch.restype = _I
+    L.bca_decode_graph_launch.argtypes = [_P, _P]
+    L.bca_decode_graph_destroy.restype = None
+    L.bca_decode_graph_destroy.argtypes = [_P]
     _lib = L
     return L
 
@@ -243,3 +251,54 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
                           _stream(dev))
     _check("bca_decode", st)
     return out, lse
+
+
+class DecodeGraph:
+    """``steps`` decode calls captured once into a HIP graph (bca_decode_graph_*).
+
+    The graph reads q, k, v and writes out, lse on every launch; write new
+    contents into those same tensors between launches.  The tensors are kept
+    alive by this object.
+    """
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, steps: int,
+                 scale: Optional[float] = None, num_splits: int = 0,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None):
+        dev = _need_gpu(q, k, v, workspace, out, lse)
+        q_len, hq, d = q.shape
+        kv_len, hkv = k.shape[0], k.shape[1]
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self.out = torch.empty_like(q) if out is None else out
+        self.lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev) if lse is None else lse
+        self._keep = (q, k, v, workspace)
+        self._dev = dev
+        self._handle = _P()
+        st = lib().bca_decode_graph_create(_ptr(q), _ptr(k), _ptr(v), _ptr(self.out),
+                                           _ptr(self.lse), q_len, kv_len, hq, hkv, d, scale,
+                                           _dtype_code(q), int(num_splits), _ptr(workspace),
+                                           ws_bytes, int(steps), ctypes.byref(self._handle))
+        _check("bca_decode_graph_create", st)
+        self.steps = int(steps)
+
+    def launch(self) -> None:
+        """Enqueue one replay (all steps) on torch's current stream."""
+        _check("bca_decode_graph_launch",
+               lib().bca_decode_graph_launch(self._handle, _stream(self._dev)))
+
+    def close(self) -> None:
+        """Release the graph after synchronising its device."""
+        if self._handle:
+            torch.cuda.synchronize(self._dev)
+            lib().bca_decode_graph_destroy(self._handle)
+            self._handle = _P()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

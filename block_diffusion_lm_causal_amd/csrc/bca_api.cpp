@@ -31,7 +31,8 @@ bca_status_t hip_status(hipError_t err, const char* what) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxDecodeSplits = 256;  // the combine kernel stages one weight per split and row
+constexpr int kMaxDecodeSplits = 256;
+constexpr int kMaxGraphSteps = 4096;  // decode steps one captured graph may hold  // the combine kernel stages one weight per split and row
 
 // Checks shared by the packed-segment entry points.
 bca_status_t check_packed(const void* q, const void* k, const void* v, const void* o,
@@ -221,11 +222,14 @@ size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t h
   return po + pl;
 }
 
-bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
-                        float scale, bca_dtype_t dtype, int32_t num_splits, void* workspace,
-                        size_t ws_bytes, void* stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+// Checks of a decode call and the kernel arguments it maps to (shared by the
+// direct call and the captured loop).
+static bca_status_t decode_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                                float scale, bca_dtype_t dtype, int32_t num_splits,
+                                void* workspace, size_t ws_bytes, bca::DecodeArgs* a) {
   if (q_len < 1 || kv_len < q_len)
     return fail(BCA_ERR_SHAPE, "need 1 <= q_len (%d) <= kv_len (%d)", q_len, kv_len);
   if (hq <= 0 || hkv <= 0 || hq % hkv)
@@ -243,25 +247,99 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (need > 0 && !aligned16(workspace)) return fail(BCA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  bca::DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
+  a->q = static_cast<const uint16_t*>(q);
+  a->k = static_cast<const uint16_t*>(k);
+  a->v = static_cast<const uint16_t*>(v);
+  a->o = static_cast<uint16_t*>(o);
+  a->lse = lse;
   const size_t po =
       ((size_t)ns * hq * ((q_len + 31) / 32) * 32 * d * sizeof(float) + 255) & ~(size_t)255;
-  a.part_o = ns > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
-  a.q_len = q_len;
-  a.kv_len = kv_len;
-  a.hq = hq;
-  a.hkv = hkv;
-  a.d = d;
-  a.hpw = bca::heads_per_wg(hq, hkv);
-  a.nsplit = ns;
-  a.scale_log2 = scale * kLog2e;
+  a->part_o = ns > 1 ? static_cast<float*>(workspace) : nullptr;
+  a->part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
+  a->q_len = q_len;
+  a->kv_len = kv_len;
+  a->hq = hq;
+  a->hkv = hkv;
+  a->d = d;
+  a->hpw = bca::heads_per_wg(hq, hkv);
+  a->nsplit = ns;
+  a->scale_log2 = scale * kLog2e;
+  return BCA_OK;
+}
+
+struct bca_decode_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  int32_t steps;
+};
+
+extern "C" {
+
+bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                        float scale, bca_dtype_t dtype, int32_t num_splits, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  bca::DecodeArgs a;
+  const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
+                                      num_splits, workspace, ws_bytes, &a);
+  if (st != BCA_OK) return st;
   return hip_status(bca::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t q_len, int32_t kv_len, int32_t hq,
+                                     int32_t hkv, int32_t d, float scale, bca_dtype_t dtype,
+                                     int32_t num_splits, void* workspace, size_t ws_bytes,
+                                     int32_t steps, bca_decode_graph_t** graph) {
+  g_last_error[0] = '\0';
+  if (!graph) return fail(BCA_ERR_NULL, "graph handle pointer is NULL");
+  *graph = nullptr;
+  if (steps < 1 || steps > kMaxGraphSteps)
+    return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
+  bca::DecodeArgs a;
+  const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
+                                      num_splits, workspace, ws_bytes, &a);
+  if (st != BCA_OK) return st;
+  hipStream_t s = nullptr;
+  hipError_t err = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (err != hipSuccess) return hip_status(err, "capture stream");
+  err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (err != hipSuccess) {
+    (void)hipStreamDestroy(s);
+    return hip_status(err, "begin capture");
+  }
+  hipError_t launch_err = hipSuccess;
+  for (int32_t i = 0; i < steps && launch_err == hipSuccess; ++i)
+    launch_err = bca::launch_decode_bf16(a, s);
+  hipGraph_t g = nullptr;
+  err = hipStreamEndCapture(s, &g);
+  (void)hipStreamDestroy(s);
+  if (launch_err != hipSuccess || err != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return hip_status(launch_err != hipSuccess ? launch_err : err, "decode capture");
+  }
+  hipGraphExec_t exec = nullptr;
+  err = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  if (err != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_status(err, "graph instantiate");
+  }
+  *graph = new bca_decode_graph{g, exec, steps};
+  return BCA_OK;
+}
+
+bca_status_t bca_decode_graph_launch(bca_decode_graph_t* graph, void* stream) {
+  g_last_error[0] = '\0';
+  if (!graph) return fail(BCA_ERR_NULL, "graph handle is NULL");
+  return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "graph launch");
+}
+
+void bca_decode_graph_destroy(bca_decode_graph_t* graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
 }
 
 }  // extern "C"

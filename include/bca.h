@@ -167,6 +167,38 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
                         float scale, bca_dtype_t dtype, int32_t num_splits, void* workspace,
                         size_t ws_bytes, void* stream);
 
+/*
+ * Captured denoising loop (thread page, Result 4: each block's denoising loop
+ * runs on the GPU as one captured graph, so per-step launch and scheduling
+ * costs vanish at batch 1).  bca_decode_graph_create checks its arguments as
+ * bca_decode does, then records `steps` consecutive bca_decode calls on these
+ * buffers into a HIP graph (through a private capture stream) and
+ * instantiates it.  Each bca_decode_graph_launch enqueues one replay of all
+ * `steps` calls on `stream`, ordered after earlier work on that stream.
+ *   steps  : 1 .. 4096
+ *   graph  : receives an opaque handle (set to NULL on failure)
+ * The graph keeps the raw pointers: the buffers (workspace included) must
+ * stay allocated, at the same addresses and sizes, until the graph is
+ * destroyed; their contents may change between launches (the caller writes a
+ * step's new queries or the block's own K/V rows, then launches).  Replays of
+ * one graph that overlap (two streams) race on o, lse and the workspace.
+ * Unlike the other entry points, create allocates the HIP runtime's graph
+ * objects; it allocates no device buffer of its own.  Launch and destroy do
+ * not synchronise; destroy a graph only after its last replay has finished.
+ */
+typedef struct bca_decode_graph bca_decode_graph_t;
+
+bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t q_len, int32_t kv_len, int32_t hq,
+                                     int32_t hkv, int32_t d, float scale, bca_dtype_t dtype,
+                                     int32_t num_splits, void* workspace, size_t ws_bytes,
+                                     int32_t steps, bca_decode_graph_t** graph);
+
+bca_status_t bca_decode_graph_launch(bca_decode_graph_t* graph, void* stream);
+
+/* Releases the graph (NULL is ignored). */
+void bca_decode_graph_destroy(bca_decode_graph_t* graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,3 +136,20 @@ def test_binding_requires_gpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(bca.BcaError):
         bca.fwd(q, q, q, cu, 2)
+
+
+def test_decode_graph_checks(L):
+    h = ctypes.c_void_p()
+    need = L.bca_decode_workspace(32, 1056, 32, 8, 128, 0)
+
+    def create(steps=4, dt=BF16, ws=FAKE, handle=ctypes.byref(h), q=FAKE):
+        return L.bca_decode_graph_create(q, FAKE, FAKE, FAKE, FAKE, 32, 1056, 32, 8, 128, 0.088,
+                                         dt, 0, ws, need, steps, handle)
+    assert create(steps=0) == SHAPE and not h.value
+    assert create(steps=5000) == SHAPE
+    assert create(dt=F32) == DTYPE
+    assert create(ws=None) == WS
+    assert create(q=None) == NULL
+    assert create(handle=None) == NULL
+    L.bca_decode_graph_destroy(None)  # no-op
+    assert L.bca_decode_graph_launch(None, None) == NULL
