@@ -17,13 +17,14 @@ under ``"paths"``:
     graph (caches warm), labelled;
   * staircase forward, 8 packed trajectories (block 32);
   * staircase forward and backward, 16 packed trajectories (block 64),
-    backward FLOPs counted as 10 * d per admitted pair per query head.
+    backward FLOPs counted as 10 * d per admitted pair per query head;
+  * compute-balanced packing of trajectories into bins (host routine).
 
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 headline workload (whole query heads until about 10 s have elapsed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-       [--only-headline] [--paths decode,staircase] [--copy-calibration]
+       [--only-headline] [--paths decode,staircase,packing] [--copy-calibration]
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -209,6 +210,27 @@ def bench_staircase(workload_fn, steps: int, warmup: int, backward: bool):
     return res
 
 
+def bench_packing():
+    """Compute-balanced packing (host): balance of the 16-trajectory workload
+    over 8 bins, and the time to pack 10,000 random trajectories."""
+    import numpy as np
+    from block_diffusion_lm_causal_amd import bca, workloads
+    w = workloads.staircase_bwd_16traj()
+    lens = np.diff(w.cu_seqlens)
+    _, cost, _, _ = bca.pack_balanced(lens, w.s_copies, w.block_size, 8)
+    rng = np.random.default_rng(5)
+    B = 64
+    prefix = B * rng.integers(16, 129, size=10000)
+    copies = rng.integers(4, 25, size=10000)
+    t0 = time.perf_counter()
+    _, cost_big, _, _ = bca.pack_balanced(prefix + copies * B, copies, B, 64)
+    pack_us = (time.perf_counter() - t0) * 1e6
+    return {"workload": "16 trajectories into 8 bins; 10,000 random trajectories into 64 bins",
+            "max_over_mean_cost_16traj_8bins": round(float(cost.max() / cost.mean()), 4),
+            "max_over_mean_cost_10k_64bins": round(float(cost_big.max() / cost_big.mean()), 6),
+            "host_us_10k_trajectories": round(pack_us, 1)}
+
+
 def cpu_baseline(budget_s: float = 10.0):
     """The fp64 oracle on whole query heads of the headline workload until the
     budget is spent (at least one head)."""
@@ -243,8 +265,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline case only")
-    ap.add_argument("--paths", default="decode,staircase",
-                    help="comma list of extra paths to time: decode, staircase (or none)")
+    ap.add_argument("--paths", default="decode,staircase,packing",
+                    help="comma list of extra paths to time: decode, staircase, packing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (a known-size "
                          "kernel against which HBM byte counters are scaled)")
@@ -288,6 +310,8 @@ def main() -> int:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")
             paths[f"decode_P{P}"] = bench_decode(P)
+    if "packing" in extra:
+        paths["packing"] = bench_packing()
     if "staircase" in extra:
         log("[bench] staircase forward, 8 trajectories")
         paths["staircase_fwd_8traj"] = bench_staircase(workloads.staircase_fwd_8traj,

@@ -26,6 +26,7 @@ EXPORTS = (
     "bca_abi_version", "bca_status_string", "bca_last_error", "bca_fwd", "bca_staircase_fwd",
     "bca_staircase_bwd_workspace", "bca_staircase_bwd", "bca_decode_workspace", "bca_decode",
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
+    "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
 )
 
 
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_graph_launch.argtypes = [_P, _P]
     L.bca_decode_graph_destroy.restype = None
     L.bca_decode_graph_destroy.argtypes = [_P]
+    L.bca_trajectory_cost.restype = ctypes.c_int64
+    L.bca_trajectory_cost.argtypes = [_I, _I, _I]
+    L.bca_pack_balanced.restype = _I
+    L.bca_pack_balanced.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P]
+    L.bca_pack_last_error.restype = ctypes.c_char_p
+    L.bca_pack_last_error.argtypes = []
     _lib = L
     return L
 
@@ -302,3 +309,32 @@ class DecodeGraph:
             self.close()
         except Exception:
             pass
+
+
+def trajectory_cost(seqlen: int, s_copies: int, block_size: int) -> int:
+    """Admitted (query, key) pairs per query head of one trajectory (-1 if invalid)."""
+    return int(lib().bca_trajectory_cost(int(seqlen), int(s_copies), int(block_size)))
+
+
+def pack_balanced(seqlens, s_copies, block_size: int, nbins: int):
+    """Compute-balanced assignment of trajectories to ``nbins`` bins (host only).
+
+    Returns numpy arrays (bin_of [ntraj], bin_cost [nbins], order [ntraj],
+    bin_start [nbins + 1]); bin b holds order[bin_start[b]:bin_start[b+1]].
+    """
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    sc = None if s_copies is None else np.ascontiguousarray(np.asarray(s_copies, dtype=np.int32))
+    n = int(sl.shape[0])
+    if sc is not None and sc.shape[0] != n:
+        raise BcaError("bca_pack_balanced", 2, "s_copies must have one entry per trajectory")
+    bin_of = np.zeros(n, dtype=np.int32)
+    bin_cost = np.zeros(max(int(nbins), 1), dtype=np.int64)
+    order = np.zeros(n, dtype=np.int32)
+    bin_start = np.zeros(max(int(nbins), 1) + 1, dtype=np.int32)
+    vp = lambda a: None if a is None else a.ctypes.data_as(_P)
+    st = lib().bca_pack_balanced(vp(sl), vp(sc), n, int(block_size), int(nbins), vp(bin_of),
+                                 vp(bin_cost), vp(order), vp(bin_start))
+    if st != 0:
+        raise BcaError("bca_pack_balanced", st, lib().bca_pack_last_error().decode())
+    return bin_of, bin_cost, order, bin_start

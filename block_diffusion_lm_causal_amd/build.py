@@ -22,6 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = [
     "bca_api.cpp",
+    "bca_pack.cpp",
     "attn_fwd_bf16.hip",
     "attn_fwd_f32.hip",
     "attn_bwd_bf16.hip",

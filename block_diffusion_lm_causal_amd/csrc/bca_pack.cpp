@@ -1,0 +1,88 @@
+// Compute-balanced packing of staircase trajectories (host code).
+//
+// "On-Policy Residual Learning for Diffusion Language Models" (paper cards
+// page, abstract and Figure 3 caption; thread page, Insight 3): captured
+// trajectories are packed and balanced by compute across GPUs (or across the
+// micro-batches of one GPU) before replay.  The cost of a trajectory is the
+// number of (query, key) pairs its attention admits per query head, in closed
+// form from its length L, copies S and block size B (P = L - S B):
+//   prefix of n = P / B whole blocks and r = P % B tokens:
+//     B^2 n (n + 1) / 2 + r (n B + r)
+//   S copies of one block, each seeing the prefix and itself:  S B (P + B)
+// Forward and backward FLOPs are both proportional to it.  Trajectories are
+// assigned greedily in order of decreasing cost (ties: lower index first) to
+// the bin with the least cost so far (ties: lower bin first) -- the
+// longest-processing-time rule, whose largest bin is within 4/3 - 1/(3 nbins)
+// of the best possible.
+#include <cstdint>
+#include <cstdio>
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "../../include/bca.h"
+
+namespace {
+
+thread_local char g_pack_error[256] = "";
+
+bca_status_t pack_fail(bca_status_t st, const char* msg, long long a, long long b) {
+  snprintf(g_pack_error, sizeof(g_pack_error), msg, a, b);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bca_trajectory_cost(int32_t seqlen, int32_t s_copies, int32_t block_size) {
+  if (seqlen < 0 || s_copies < 0 || block_size < 1) return -1;
+  const int64_t L = seqlen, S = s_copies, B = block_size;
+  const int64_t P = L - S * B;
+  if (P < 0 || (S > 0 && P % B != 0)) return -1;
+  const int64_t n = P / B, r = P % B;
+  return B * B * n * (n + 1) / 2 + r * (n * B + r) + S * B * (P + B);
+}
+
+bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, int32_t ntraj,
+                               int32_t block_size, int32_t nbins, int32_t* bin_of,
+                               int64_t* bin_cost, int32_t* order, int32_t* bin_start) {
+  g_pack_error[0] = '\0';
+  if (ntraj < 0 || nbins < 1 || block_size < 1)
+    return pack_fail(BCA_ERR_SHAPE, "need ntraj >= 0 (%lld), nbins >= 1 (%lld), block_size >= 1",
+                     ntraj, nbins);
+  if (ntraj > 0 && (!seqlens || !bin_of || !order)) return pack_fail(BCA_ERR_NULL, "a required pointer is NULL", 0, 0);
+  if (!bin_cost || !bin_start) return pack_fail(BCA_ERR_NULL, "a required pointer is NULL", 0, 0);
+  std::vector<int64_t> cost(ntraj);
+  for (int32_t t = 0; t < ntraj; ++t) {
+    const int32_t S = s_copies ? s_copies[t] : 0;
+    cost[t] = bca_trajectory_cost(seqlens[t], S, block_size);
+    if (cost[t] < 0)
+      return pack_fail(BCA_ERR_SHAPE, "trajectory %lld: bad length %lld for its copies and block size",
+                       t, seqlens[t]);
+  }
+  std::vector<int32_t> by_cost(ntraj);
+  std::iota(by_cost.begin(), by_cost.end(), 0);
+  std::stable_sort(by_cost.begin(), by_cost.end(),
+                   [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+  for (int32_t b = 0; b < nbins; ++b) bin_cost[b] = 0;
+  std::vector<int32_t> count(nbins, 0);
+  for (int32_t t : by_cost) {
+    int32_t best = 0;
+    for (int32_t b = 1; b < nbins; ++b)
+      if (bin_cost[b] < bin_cost[best]) best = b;
+    bin_of[t] = best;
+    bin_cost[best] += cost[t];
+    ++count[best];
+  }
+  // members of each bin, in assignment order (costliest first)
+  bin_start[0] = 0;
+  for (int32_t b = 0; b < nbins; ++b) bin_start[b + 1] = bin_start[b] + count[b];
+  std::vector<int32_t> fill(bin_start, bin_start + nbins);
+  for (int32_t t : by_cost) order[fill[bin_of[t]]++] = t;
+  return BCA_OK;
+}
+
+const char* bca_pack_last_error(void) { return g_pack_error; }
+
+}  // extern "C"

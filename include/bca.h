@@ -199,6 +199,41 @@ bca_status_t bca_decode_graph_launch(bca_decode_graph_t* graph, void* stream);
 /* Releases the graph (NULL is ignored). */
 void bca_decode_graph_destroy(bca_decode_graph_t* graph);
 
+/*
+ * Compute-balanced packing (paper cards page, abstract and Figure 3 caption:
+ * captured states are packed and balanced by compute across GPUs; thread
+ * page, Insight 3).  Host-only: these calls touch no GPU and may run anywhere.
+ *
+ * bca_trajectory_cost: pairs of (query, key) admitted per query head by one
+ * trajectory of `seqlen` tokens with `s_copies` copies of its last block:
+ * with P = seqlen - s_copies * B, n = P / B, r = P % B,
+ *   B^2 n (n+1) / 2 + r (n B + r) + s_copies * B * (P + B).
+ * Returns -1 for invalid arguments (P < 0, or P % B != 0 with copies).
+ */
+int64_t bca_trajectory_cost(int32_t seqlen, int32_t s_copies, int32_t block_size);
+
+/*
+ * Assigns `ntraj` trajectories to `nbins` bins so that the largest bin cost
+ * stays small: longest-processing-time greedy -- trajectories by decreasing
+ * cost (ties: lower index first), each to the bin of least cost so far (ties:
+ * lower bin index).  All arrays are host memory owned by the caller:
+ *   seqlens   : [ntraj] lengths in tokens;  s_copies : [ntraj] or NULL (all 0)
+ *   bin_of    : out [ntraj], the bin of each trajectory
+ *   bin_cost  : out [nbins], summed costs
+ *   order     : out [ntraj], trajectory indices grouped by bin, each bin's in
+ *               assignment order (costliest first)
+ *   bin_start : out [nbins + 1], bin b's members are order[bin_start[b] ..
+ *               bin_start[b+1])
+ * Errors: BCA_ERR_SHAPE (ntraj < 0, nbins < 1, block_size < 1, a bad
+ * trajectory), BCA_ERR_NULL; bca_pack_last_error() gives the message.
+ */
+bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, int32_t ntraj,
+                               int32_t block_size, int32_t nbins, int32_t* bin_of,
+                               int64_t* bin_cost, int32_t* order, int32_t* bin_start);
+
+/* Message of the calling thread's last packing failure ("" if none). */
+const char* bca_pack_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

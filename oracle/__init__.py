@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
 CPU-baseline leg of the benchmark, never by the product path.  It shares no
 code with the HIP library (see ``attention.py`` for what it computes and the
-passages it follows).
+passages it follows; ``packing.py`` holds the compute-balanced packing rule).
 
 Every function here is pinned by ``tests/test_oracle.py`` against facts that
 do not come from the oracle itself: torch's fp64 scaled-dot-product attention
@@ -13,6 +13,7 @@ and torch autograd for the gradients, and the invariants of softmax attention.
 """
 from .attention import (allowed_matrix, attention_bwd, attention_dq_rows, attention_fwd,
                         decode, segment_prefix_len)
+from .packing import lpt, optimal_makespan, trajectory_cost
 
 __all__ = ["allowed_matrix", "attention_bwd", "attention_dq_rows", "attention_fwd", "decode",
-           "segment_prefix_len"]
+           "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost"]

@@ -1,0 +1,134 @@
+"""Compute-balanced packing: the oracle's rule pinned to textbook facts, the
+library's host routine against the oracle (exact, integers), and the packed
+output consumed by the staircase forward on the GPU.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_lm_causal_amd import bca
+from block_diffusion_lm_causal_amd import workloads as W
+
+from gpu_helpers import device_inputs
+
+
+def lib_or_skip():
+    import os
+    if not os.path.exists(bca.LIB_PATH):
+        pytest.skip("libbca.so not built")
+    return bca.lib()
+
+
+# --- the oracle's rule, pinned ---------------------------------------------
+
+def test_lpt_textbook_instance():
+    # Graham's instance: jobs 3,3,2,2,2 on two machines.  The greedy rule puts
+    # 3 | 3, then 2 on the first (tie -> lower machine), 2 on the second, 2 on
+    # the first: loads 7 and 5, while 6 | 6 ({3,3}, {2,2,2}) is optimal.
+    bin_of, bin_cost, order, start = oracle.lpt([3, 3, 2, 2, 2], 2)
+    assert bin_of.tolist() == [0, 1, 0, 1, 0]
+    assert bin_cost.tolist() == [7, 5]
+    assert order.tolist() == [0, 2, 4, 1, 3] and start.tolist() == [0, 3, 5]
+    assert oracle.optimal_makespan([3, 3, 2, 2, 2], 2) == 6
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_lpt_within_graham_bound(seed):
+    rng = np.random.default_rng(seed)
+    n, m = int(rng.integers(1, 8)), int(rng.integers(1, 4))
+    costs = rng.integers(1, 50, size=n).tolist()
+    _, bin_cost, order, start = oracle.lpt(costs, m)
+    opt = oracle.optimal_makespan(costs, m)
+    assert sum(bin_cost) == sum(costs)
+    assert sorted(order.tolist()) == list(range(n)) and start[-1] == n
+    assert max(bin_cost) * 3 * m <= (4 * m - 1) * opt     # <= (4/3 - 1/(3m)) OPT
+    assert max(bin_cost) >= opt
+
+
+def test_optimal_makespan_brute_force_small():
+    # an exact split exists: 5+4 = 6+3 = 9
+    assert oracle.optimal_makespan([6, 5, 4, 3], 2) == 9
+    assert oracle.optimal_makespan([7], 3) == 7
+    assert oracle.optimal_makespan([], 2) == 0
+
+
+# --- the library against the oracle -----------------------------------------
+
+@pytest.mark.parametrize("L,S,B", [(10, 3, 2), (7, 0, 3), (96, 2, 16), (64, 0, 64), (40, 5, 8),
+                                   (33, 0, 32), (0, 0, 4), (48, 6, 8)])
+def test_trajectory_cost_counts_the_mask(L, S, B):
+    lib_or_skip()
+    want = oracle.trajectory_cost(L, S, B)
+    assert bca.trajectory_cost(L, S, B) == want
+    assert W.useful_pairs([L], [S], B) == want
+
+
+def test_trajectory_cost_rejects_bad_shapes():
+    lib_or_skip()
+    assert bca.trajectory_cost(10, 3, 4) == -1      # P = -2
+    assert bca.trajectory_cost(13, 2, 4) == -1      # P = 5 is not whole blocks
+    assert bca.trajectory_cost(5, 0, 0) == -1
+
+
+@pytest.mark.parametrize("seed,n,m", [(0, 16, 8), (1, 8, 3), (2, 30, 4), (3, 3, 5), (4, 1, 1),
+                                      (5, 50, 7), (6, 0, 2)])
+def test_pack_matches_oracle(seed, n, m):
+    lib_or_skip()
+    rng = np.random.default_rng(seed)
+    B = 8
+    prefix = B * rng.integers(0, 12, size=n)
+    copies = rng.integers(0, 5, size=n)
+    # a few exact cost ties
+    if n >= 4:
+        prefix[1], copies[1] = prefix[0], copies[0]
+        prefix[3], copies[3] = prefix[2], copies[2]
+    seqlens = prefix + copies * B
+    got = bca.pack_balanced(seqlens, copies, B, m)
+    costs = [oracle.trajectory_cost(int(L), int(S), B) for L, S in zip(seqlens, copies)]
+    want = oracle.lpt(costs, m)
+    for g, w_ in zip(got, want):
+        assert np.array_equal(g, w_), (g, w_)
+
+
+def test_pack_rejects_bad_input():
+    lib_or_skip()
+    with pytest.raises(bca.BcaError):
+        bca.pack_balanced([10], [3], 4, 2)       # P < 0
+    with pytest.raises(bca.BcaError):
+        bca.pack_balanced([8], [0], 4, 0)        # no bins
+
+
+# --- a GPU consumer of the packed output ----------------------------------
+
+@pytest.mark.gpu
+def test_packed_bins_reproduce_the_full_batch():
+    """Repacking the 8 trajectories into 3 balanced bins and running each bin
+    alone gives every trajectory bit-identical O and LSE rows."""
+    w = W.staircase_fwd_8traj()
+    q, k, v, cu, sc, _ = device_inputs(w)
+    o_all, lse_all = bca.staircase_fwd(q, k, v, cu, sc, w.block_size, w.scale, w.max_seqlen)
+    lens = np.diff(w.cu_seqlens)
+    bin_of, bin_cost, order, start = bca.pack_balanced(lens, w.s_copies, w.block_size, 3)
+    costs = [bca.trajectory_cost(int(L), int(S), w.block_size) for L, S in zip(lens, w.s_copies)]
+    assert max(bin_cost) * 9 <= 11 * oracle.optimal_makespan(costs, 3)  # LPT bound, m = 3
+    for b in range(3):
+        members = order[start[b]:start[b + 1]].tolist()
+        if not members:
+            continue
+        rows = [torch.arange(int(w.cu_seqlens[t]), int(w.cu_seqlens[t + 1]), device=q.device)
+                for t in members]
+        idx = torch.cat(rows)
+        cu_b = torch.tensor(np.concatenate([[0], np.cumsum([len(r) for r in rows])]),
+                            dtype=torch.int32, device=q.device)
+        sc_b = torch.tensor([int(w.s_copies[t]) for t in members], dtype=torch.int32,
+                            device=q.device)
+        max_len = max(len(r) for r in rows)
+        o_b, lse_b = bca.staircase_fwd(q[idx].contiguous(), k[idx].contiguous(),
+                                       v[idx].contiguous(), cu_b, sc_b, w.block_size, w.scale,
+                                       max_len)
+        torch.cuda.synchronize()
+        assert torch.equal(o_b, o_all[idx])
+        assert torch.equal(lse_b, lse_all[:, idx])
