@@ -172,10 +172,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const int c = (lane % kChunks) ^ swz<D>(R);
     dma_voff[j] = (uint32_t)(R * q_row_elems * 2 + c * 16);
   }
-  auto step_qt0 = [&](int st) { return qs + (nqt - 1 - st / group) * kQt; };
-  auto issue_step = [&](int st, int buf) {
-    const int qt0 = step_qt0(st);
-    const int head = g * group + st % group;
+  // Step st covers query tile nqt-1-st/group (tiles swept from the last one
+  // down) of query head g*group + st%group.  Steps are walked with cursors
+  // (first row of the tile, head within the group) instead of divisions.
+  struct Cursor {
+    int qt0, h;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.h == group) {
+      c.h = 0;
+      c.qt0 -= kQt;
+    }
+  };
+  auto issue_step = [&](const Cursor& c, int buf) {
+    const int qt0 = c.qt0;
+    const int head = g * group + c.h;
     const int rows = min(qe - qt0, kQt);
     const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
     const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
@@ -193,10 +204,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     if (wave == 0) wait_vmem_le<kDmaPerWave + 1>();
     else wait_vmem_le<kDmaPerWave>();
   };
-  auto load_side = [&](int st) -> float {
+  auto load_side = [&](const Cursor& c) -> float {
     // wave 0: lanes 0-31 the LSE of the tile's rows (scaled by log2 e), 32-63 delta
-    const int qt0 = step_qt0(st);
-    const int head = g * group + st % group;
+    const int qt0 = c.qt0;
+    const int head = g * group + c.h;
     const int i = qt0 + (lane & 31);
     float v = 0.f;
     if (i < qe) {
@@ -239,44 +250,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 
   const int wave_key_last = min(kw0 + 31, L - 1);
   const bool wave_has_keys = kw0 < L;
+  // Rows admitting this lane's key, and for the wave: rows admitting any of
+  // its keys [wave_lo, wave_hi) and rows admitting all 32 of them
+  // [full_lo, full_hi).  Row intervals start later for later keys; a prefix
+  // key's interval ends at L, a copy key's at the end of its copy.
+  KeyRows kr = KeyRows{0, 0};
+  if (key < L) kr = key_rows(key, P, L, B);
+  int wave_lo = 0, wave_hi = 0, full_lo = 0, full_hi = 0;
+  if (wave_has_keys) {
+    const KeyRows first = key_rows(kw0, P, L, B), last = key_rows(wave_key_last, P, L, B);
+    wave_lo = first.lo;
+    wave_hi = kw0 < P ? L : last.hi;
+    full_lo = last.lo;
+    full_hi = wave_key_last >= P ? key_rows(kw0 > P ? kw0 : P, P, L, B).hi : L;
+    if (kw0 + 31 >= L) full_hi = 0;  // a wave with padding keys is never full
+  }
 
   // Prologue: steps 0 and 1 in flight, step 0's side values in LDS.
+  Cursor cur = Cursor{qs + (nqt - 1) * kQt, 0};  // step st
+  Cursor nxt = cur;                              // step st + 2
   float side_next = 0.f, side_new = 0.f;
   if (nsteps > 0) {
-    if (wave == 0) store_side(load_side(0), 0);
-    issue_step(0, 0);
+    if (wave == 0) store_side(load_side(nxt), 0);
+    issue_step(nxt, 0);
+    advance(nxt);
     if (nsteps > 1) {
-      if (wave == 0) side_next = load_side(1);
-      issue_step(1, 1);
+      if (wave == 0) side_next = load_side(nxt);
+      issue_step(nxt, 1);
+      advance(nxt);
     }
   }
   if (nsteps > 1) wait_all_but_newest();  // step 0's tile landed (step 1's may remain)
   else wait_vmem();
   __syncthreads();
 
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st % 3;
+  for (int st = 0, buf = 0; st < nsteps; ++st, buf = buf == 2 ? 0 : buf + 1) {
     if (st + 2 < nsteps) {
-      if (wave == 0) side_new = load_side(st + 2);
-      issue_step(st + 2, (st + 2) % 3);
+      const int buf2 = buf == 0 ? 2 : buf - 1;  // (st + 2) % 3
+      if (wave == 0) side_new = load_side(nxt);
+      issue_step(nxt, buf2);
+      advance(nxt);
     }
-    const int qt0 = step_qt0(st);
-    // Does any row of this query tile admit any key of this wave?
-    const int qa = qt0, qb = min(qt0 + kQt, qe) - 1;
-    const RowKeys ra = row_keys(qa, P, L, B);
-    const RowKeys rb = row_keys(qb, P, L, B);
-    bool active = wave_has_keys;
+    const int qt0 = cur.qt0;
+    const bool active = wave_has_keys && qt0 < wave_hi && qt0 + kQt > wave_lo;
     if (active) {
-      const bool hits_prefix = kw0 < rb.e1;
-      const int first_copy_row = qa > P ? qa : P;
-      const bool hits_copy = qb >= P && kw0 < rb.e2 &&
-                             wave_key_last >= row_keys(first_copy_row, P, L, B).s2;
-      active = hits_prefix || hits_copy;
-    }
-    if (active) {
-      const bool full = qt0 + kQt <= qe && kw0 + 31 < L &&
-                        ((kw0 + 31 < ra.e1) ||
-                         (ra.e2 > ra.s2 && ra.s2 == rb.s2 && kw0 >= ra.s2 && kw0 + 31 < ra.e2));
+      const bool full = qt0 + kQt <= qe && qt0 >= full_lo && qt0 + kQt <= full_hi;
       const char* qtile = reinterpret_cast<const char*>(lds.q[buf]);
       const char* gtile = reinterpret_cast<const char*>(lds.g[buf]);
       // S = Q K^T (and dP = dO V^T in K waves): queries on M, keys on N.
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
           float pv = fast_exp2(fmaf(s[r], a.scale_log2, -l2[e]));
           if (!full) {
             const int i = qt0 + q0r + e;
-            const bool ok = (i < qe) & (key < L) & admitted(row_keys(i, P, L, B), key);
+            const bool ok = (i < qe) & (i >= kr.lo) & (i < kr.hi);
             pv = ok ? pv : 0.f;
           }
           v[e] = kwave ? pv * (dp[r] - dl[e]) : pv;
@@ -330,15 +348,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
         }
       }
     }
+    advance(cur);
     // Step st+1's tile must have landed; step st+2's may still be in flight.
+    const int buf1 = buf == 2 ? 0 : buf + 1;
     if (st + 2 < nsteps) {
       if (wave == 0) {
-        store_side(side_next, (st + 1) % 3);
+        store_side(side_next, buf1);
         side_next = side_new;
       }
       wait_all_but_newest();
     } else {
-      if (wave == 0 && st + 1 < nsteps) store_side(side_next, (st + 1) % 3);
+      if (wave == 0 && st + 1 < nsteps) store_side(side_next, buf1);
       wait_vmem();
     }
     __syncthreads();

@@ -130,6 +130,28 @@ __device__ __forceinline__ bool admitted(const RowKeys& r, int j) {
   return j < r.e1 || (j >= r.s2 && j < r.e2);
 }
 
+// The query rows that admit key j (0 <= j < L), which always form one
+// interval [lo, hi): a prefix key of block floor(j/B) is seen by the prefix
+// rows of that block and later ones and by every copy row; a key of copy c
+// only by the rows of copy c.
+struct KeyRows {
+  int lo, hi;
+};
+
+__device__ __forceinline__ KeyRows key_rows(int j, int P, int L, int B) {
+  KeyRows r;
+  if (j < P) {
+    r.lo = (j / B) * B;
+    r.hi = L;
+  } else {
+    const int c = (j - P) / B;
+    const int e = P + (c + 1) * B;
+    r.lo = P + c * B;
+    r.hi = e < L ? e : L;
+  }
+  return r;
+}
+
 // Key ranges a tile of query rows [q_first, q_last] (inclusive, all inside
 // the segment) must visit: [0, r1e) and [r2s, r2e), merged when they touch.
 struct TileKeys {
