@@ -27,6 +27,7 @@ EXPORTS = (
     "bca_staircase_bwd_workspace", "bca_staircase_bwd", "bca_decode_workspace", "bca_decode",
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
+    "bca_staircase_groups_fwd", "bca_staircase_groups_bwd",
 )
 
 
@@ -83,6 +84,12 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_graph_launch.argtypes = [_P, _P]
     L.bca_decode_graph_destroy.restype = None
     L.bca_decode_graph_destroy.argtypes = [_P]
+    L.bca_staircase_groups_fwd.restype = _I
+    L.bca_staircase_groups_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                           _I, _I, _I, _F, _I, _P]
+    L.bca_staircase_groups_bwd.restype = _I
+    L.bca_staircase_groups_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]
     L.bca_trajectory_cost.restype = ctypes.c_int64
     L.bca_trajectory_cost.argtypes = [_I, _I, _I]
     L.bca_pack_balanced.restype = _I
@@ -197,6 +204,77 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
                        _stream(dev))
     _check("bca_fwd", st)
     return out, lse
+
+
+def _groups_args(func, group_start, group_pe, group_copies, nseq):
+    for t, name in ((group_start, "group_start"), (group_pe, "group_pe"),
+                    (group_copies, "group_copies")):
+        if t is None or t.dtype != torch.int32:
+            raise BcaError(func, 2, f"{name} must be an int32 tensor")
+    if group_start.numel() != nseq + 1 or group_pe.numel() != group_copies.numel():
+        raise BcaError(func, 2, "group_start must be [nseq + 1]; group_pe and group_copies "
+                                "must have one entry per group")
+
+
+def staircase_groups_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         cu_seqlens: torch.Tensor, group_start: torch.Tensor,
+                         group_pe: torch.Tensor, group_copies: torch.Tensor, block_size: int,
+                         scale: Optional[float] = None, max_seqlen: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """General trajectory staircase forward -> (O, LSE): copy groups per segment,
+    group g's copies seeing the clean keys [0, group_pe[g])."""
+    dev = _need_gpu(q, k, v, cu_seqlens, group_start, group_pe, group_copies, out, lse)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (total, hkv, d) or v.shape != k.shape:
+        raise BcaError("staircase_groups_fwd", 2, "k and v must be [total, hkv, d] matching q")
+    nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    _groups_args("staircase_groups_fwd", group_start, group_pe, group_copies, nseq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
+    st = lib().bca_staircase_groups_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _ptr(cu_seqlens), _ptr(group_start), _ptr(group_pe),
+                                        _ptr(group_copies), nseq, max_seqlen, total, hq, hkv, d,
+                                        int(block_size), scale, _dtype_code(q), _stream(dev))
+    _check("bca_staircase_groups_fwd", st)
+    return out, lse
+
+
+def staircase_groups_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                         lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor,
+                         group_start: torch.Tensor, group_pe: torch.Tensor,
+                         group_copies: torch.Tensor, block_size: int,
+                         scale: Optional[float] = None, max_seqlen: Optional[int] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                         dv: Optional[torch.Tensor] = None):
+    """General trajectory staircase backward -> (dQ, dK, dV), bf16."""
+    dev = _need_gpu(q, k, v, o, lse, dout, cu_seqlens, group_start, group_pe, group_copies,
+                    workspace, dq, dk, dv)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    _groups_args("staircase_groups_bwd", group_start, group_pe, group_copies, nseq)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = staircase_bwd_workspace(total, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().bca_staircase_groups_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _ptr(cu_seqlens), _ptr(group_start), _ptr(group_pe),
+                                        _ptr(group_copies), nseq, max_seqlen, total, hq, hkv, d,
+                                        int(block_size), scale, _dtype_code(q), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(dev))
+    _check("bca_staircase_groups_bwd", st)
+    return dq, dk, dv
 
 
 def staircase_bwd_workspace(total: int, hq: int, hkv: int, d: int) -> int:

@@ -124,9 +124,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   const int L = a.cu_seqlens[seg + 1] - base;
   const int k0 = ktile * kKvKeys;
   if (k0 >= L) return;
-  const int S = a.s_copies ? a.s_copies[seg] : 0;
-  int P = L - S * a.block_size;
-  if (P < 0) P = 0;
+  const Stair stair = make_stair(seg, L, a.block_size, a.s_copies, a.group_start, a.group_pe,
+                                 a.group_copies);
+  const int P = stair.P;
   const int B = a.block_size;
 
   const int tid = threadIdx.x;
@@ -138,18 +138,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   const int key = kw0 + (lane & 31);      // key of this lane's accumulator column
   const int k_last_wg = min(k0 + kKvKeys, L) - 1;
 
-  // Query rows that admit any key of the workgroup.
-  int qs, qe;
+  // Query rows that admit any key of the workgroup: up to two ranges,
+  // [qs1, qe1) (prefix rows from the first key's block, and the copies that
+  // own keys of the workgroup) and [qs2, qe2) (the copies of the groups that
+  // see the first clean key).
+  int qs1, qe1, qs2 = 0, qe2 = 0;
   if (k0 < P) {
-    qs = (k0 / B) * B;
-    qe = L;
+    qs1 = (k0 / B) * B;
+    qe1 = k_last_wg >= P ? min(L, P + ((k_last_wg - P) / B + 1) * B) : P;
+    qs2 = P + first_copy_seeing(stair, k0) * B;
+    qe2 = L;
+    if (qs2 <= qe1) {
+      qe1 = max(qe1, qe2);
+      qs2 = qe2 = 0;
+    }
   } else {
     const int c_first = (k0 - P) / B, c_last = (k_last_wg - P) / B;
-    qs = P + c_first * B;
-    qe = min(L, P + (c_last + 1) * B);
+    qs1 = P + c_first * B;
+    qe1 = min(L, P + (c_last + 1) * B);
   }
-  const int nqt = (qe - qs + kQt - 1) / kQt;
-  const int nsteps = nqt * group;
+  const int nqt1 = (qe1 - qs1 + kQt - 1) / kQt;
+  const int nqt2 = qe2 > qs2 ? (qe2 - qs2 + kQt - 1) / kQt : 0;
+  const int nsteps = (nqt1 + nqt2) * group;
 
   // Loads: Q and dO tiles (32 rows x D) by DMA.  A tile is kInstPerTile
   // 1 KB instructions per tensor; instruction i of the 2 * kInstPerTile is
@@ -172,22 +182,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const int c = (lane % kChunks) ^ swz<D>(R);
     dma_voff[j] = (uint32_t)(R * q_row_elems * 2 + c * 16);
   }
-  // Step st covers query tile nqt-1-st/group (tiles swept from the last one
-  // down) of query head g*group + st%group.  Steps are walked with cursors
-  // (first row of the tile, head within the group) instead of divisions.
+  // Steps sweep the query tiles of range 2, then of range 1, each from its
+  // last tile down, every tile once per query head of the group.  A cursor
+  // holds the step's tile (first row), head within the group and range
+  // [lo, end); rows of a tile past `end` are loaded as zeros and masked.
   struct Cursor {
-    int qt0, h;
+    int qt0, h, lo, end;
   };
   auto advance = [&](Cursor& c) {
     if (++c.h == group) {
       c.h = 0;
       c.qt0 -= kQt;
+      if (c.qt0 < c.lo && c.lo != qs1) {  // range 2 done: continue with range 1
+        c.qt0 = qs1 + (nqt1 - 1) * kQt;
+        c.lo = qs1;
+        c.end = qe1;
+      }
     }
   };
   auto issue_step = [&](const Cursor& c, int buf) {
     const int qt0 = c.qt0;
     const int head = g * group + c.h;
-    const int rows = min(qe - qt0, kQt);
+    const int rows = min(c.end - qt0, kQt);
     const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
     const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + off, nbytes);
@@ -210,7 +226,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const int head = g * group + c.h;
     const int i = qt0 + (lane & 31);
     float v = 0.f;
-    if (i < qe) {
+    if (i < c.end) {
       v = half == 0 ? a.lse[(size_t)head * a.total + base + i] * kLog2e
                     : a.delta[(size_t)head * a.total + base + i];
     }
@@ -250,24 +266,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 
   const int wave_key_last = min(kw0 + 31, L - 1);
   const bool wave_has_keys = kw0 < L;
-  // Rows admitting this lane's key, and for the wave: rows admitting any of
-  // its keys [wave_lo, wave_hi) and rows admitting all 32 of them
-  // [full_lo, full_hi).  Row intervals start later for later keys; a prefix
-  // key's interval ends at L, a copy key's at the end of its copy.
-  KeyRows kr = KeyRows{0, 0};
-  if (key < L) kr = key_rows(key, P, L, B);
-  int wave_lo = 0, wave_hi = 0, full_lo = 0, full_hi = 0;
+  // Rows admitting this lane's key (at most two intervals), and for the wave
+  // the rows admitting any of its keys [w1lo, w1hi) u [w2lo, w2hi) and the
+  // rows admitting all 32 of them [f1lo, f1hi) u [f2lo, f2hi).  Along the
+  // clean keys both the prefix-row interval and the run of copies seeing the
+  // key start later for later keys; a copy key is seen by its copy only.
+  KeyRows kr = KeyRows{0, 0, 0, 0};
+  if (key < L) kr = key_rows(key, stair);
+  int w1lo = 0, w1hi = 0, w2lo = 0, w2hi = 0, f1lo = 0, f1hi = 0, f2lo = 0, f2hi = 0;
   if (wave_has_keys) {
-    const KeyRows first = key_rows(kw0, P, L, B), last = key_rows(wave_key_last, P, L, B);
-    wave_lo = first.lo;
-    wave_hi = kw0 < P ? L : last.hi;
-    full_lo = last.lo;
-    full_hi = wave_key_last >= P ? key_rows(kw0 > P ? kw0 : P, P, L, B).hi : L;
-    if (kw0 + 31 >= L) full_hi = 0;  // a wave with padding keys is never full
+    const KeyRows first = key_rows(kw0, stair), last = key_rows(wave_key_last, stair);
+    if (kw0 < P) {
+      w1lo = first.lo;
+      w1hi = wave_key_last >= P ? max(first.hi, last.hi) : first.hi;  // owned copies extend it
+      w2lo = first.lo2;
+      w2hi = first.hi2;
+    } else {
+      w1lo = first.lo;
+      w1hi = last.hi;
+    }
+    const bool all_clean = wave_key_last < P;
+    const bool one_copy_keys = kw0 >= P && (kw0 - P) / B == (wave_key_last - P) / B;
+    if (kw0 + 31 < L && (all_clean || one_copy_keys)) {
+      f1lo = last.lo;
+      f1hi = last.hi;
+      f2lo = last.lo2;
+      f2hi = last.hi2;
+    }
   }
 
   // Prologue: steps 0 and 1 in flight, step 0's side values in LDS.
-  Cursor cur = Cursor{qs + (nqt - 1) * kQt, 0};  // step st
+  Cursor cur = nqt2 > 0 ? Cursor{qs2 + (nqt2 - 1) * kQt, 0, qs2, qe2}
+                        : Cursor{qs1 + (nqt1 - 1) * kQt, 0, qs1, qe1};  // step st
   Cursor nxt = cur;                              // step st + 2
   float side_next = 0.f, side_new = 0.f;
   if (nsteps > 0) {
@@ -291,10 +321,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       issue_step(nxt, buf2);
       advance(nxt);
     }
-    const int qt0 = cur.qt0;
-    const bool active = wave_has_keys && qt0 < wave_hi && qt0 + kQt > wave_lo;
+    const int qt0 = cur.qt0, qe = cur.end;
+    const bool active = wave_has_keys && ((qt0 < w1hi && qt0 + kQt > w1lo) ||
+                                          (qt0 < w2hi && qt0 + kQt > w2lo));
     if (active) {
-      const bool full = qt0 + kQt <= qe && qt0 >= full_lo && qt0 + kQt <= full_hi;
+      const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
+                                            (qt0 >= f2lo && qt0 + kQt <= f2hi));
       const char* qtile = reinterpret_cast<const char*>(lds.q[buf]);
       const char* gtile = reinterpret_cast<const char*>(lds.g[buf]);
       // S = Q K^T (and dP = dO V^T in K waves): queries on M, keys on N.
@@ -326,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
           float pv = fast_exp2(fmaf(s[r], a.scale_log2, -l2[e]));
           if (!full) {
             const int i = qt0 + q0r + e;
-            const bool ok = (i < qe) & (i >= kr.lo) & (i < kr.hi);
+            const bool ok = (i < qe) & row_sees(kr, i);
             pv = ok ? pv : 0.f;
           }
           v[e] = kwave ? pv * (dp[r] - dl[e]) : pv;
@@ -406,10 +438,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
   const int ntiles_q = (L + tok - 1) / tok;
   if (rank >= ntiles_q) return;
   const int tile = ntiles_q - 1 - rank;
-  const int S = a.s_copies ? a.s_copies[seg] : 0;
-  int P = L - S * a.block_size;
-  if (P < 0) P = 0;
-  const int B = a.block_size;
+  const Stair stair = make_stair(seg, L, a.block_size, a.s_copies, a.group_start, a.group_pe,
+                                 a.group_copies);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -420,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
   const int g = (hg * hpw) / (a.hq / a.hkv);
   const int q0 = tile * tok;
   const int q_last = min(q0 + tok, L) - 1;
-  const TileKeys tk = tile_keys(q0, q_last, P, L, B);
+  const TileKeys tk = tile_keys(q0, q_last, stair);
   const int qw0 = q0 + (wave / hpw) * 32;
   const int qi = qw0 + (lane & 31);
   const bool wave_active = qw0 < L;
@@ -476,10 +506,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
     lse2 = a.lse[(size_t)head * a.total + base + qi] * kLog2e;
     dl = a.delta[(size_t)head * a.total + base + qi];
   }
-  const RowKeys rk = row_keys(qi < L ? qi : qw_last, P, L, B);
-  const RowKeys rkA = row_keys(wave_active ? qw0 : 0, P, L, B);
-  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, P, L, B);
+  const RowKeys rk = row_keys(qi < L ? qi : qw_last, stair);
+  const RowKeys rkA = row_keys(wave_active ? qw0 : 0, stair);
+  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, stair);
   const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
+  // every row of the wave sees the clean keys [0, e1_all)
+  const int e1_all = wave_active ? min_prefix_end(qw0, qw_last, stair) : 0;
 
   uint32_t koff[D / 16];
 #pragma unroll
@@ -550,7 +582,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
         const int tv = my >> 1;
         const int k0 = tile_k0(tv), kend = tile_end(tv);
         const bool full = wave_active && (k0 + kBN <= kend) &&
-                          ((k0 + kBN <= rkA.e1) ||
+                          ((k0 + kBN <= e1_all) ||
                            (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
 #pragma unroll
         for (int h = 0; h < kBN / 32; ++h) {

@@ -49,7 +49,7 @@ struct WgPlan {
   const uint16_t* v;
   int q_rows;            // valid query rows (segment length, or q_len for decode)
   int r1s, r1e, r2s, r2e;  // key ranges to visit
-  int P, L, B;           // admitted-key rule (decode: every key below the chunk end)
+  Stair stair;           // admitted-key rule of the segment
   int qw0;               // first query row of the calling wave
 };
 
@@ -205,10 +205,12 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
     }
     qf[kk] = __builtin_bit_cast(bf16x8, raw);
   }
-  const RowKeys rk = row_keys(qi < p.q_rows ? qi : qw_last, p.P, p.L, p.B);
-  const RowKeys rkA = row_keys(p.qw0 < p.q_rows ? p.qw0 : 0, p.P, p.L, p.B);
-  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, p.P, p.L, p.B);
+  const RowKeys rk = row_keys(qi < p.q_rows ? qi : qw_last, p.stair);
+  const RowKeys rkA = row_keys(wave_active ? p.qw0 : 0, p.stair);
+  const RowKeys rkB = row_keys(wave_active ? qw_last : 0, p.stair);
   const bool one_copy = rkA.e2 > rkA.s2 && rkA.s2 == rkB.s2;
+  // every row of the wave sees the clean keys [0, e1_all)
+  const int e1_all = wave_active ? min_prefix_end(p.qw0, qw_last, p.stair) : 0;
 
   uint32_t koff[D / 16];
   {
@@ -291,7 +293,7 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
   auto softmax_phase = [&](int t) {
     const int k0 = tile_k0(t), kend = tile_end(t);
     const bool full = wave_active && (k0 + kBN <= kend) &&
-                      ((k0 + kBN <= rkA.e1) ||
+                      ((k0 + kBN <= e1_all) ||
                        (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
     if (!full) {
 #pragma unroll
@@ -398,16 +400,15 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a, int nt
   const int ntiles = (L + tok - 1) / tok;
   if (rank >= ntiles) return;
   const int tile = ntiles - 1 - rank;
-  const int S = a.s_copies ? a.s_copies[seg] : 0;
-  int P = L - S * a.block_size;
-  if (P < 0) P = 0;
+  const Stair stair = make_stair(seg, L, a.block_size, a.s_copies, a.group_start, a.group_pe,
+                                 a.group_copies);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head = hg * a.hpw + wave % a.hpw;
   const int kv_head = (hg * a.hpw) / (a.hq / a.hkv);
   const int q0 = tile * tok;
   const int q_last = min(q0 + tok, L) - 1;
-  const TileKeys tk = tile_keys(q0, q_last, P, L, a.block_size);
+  const TileKeys tk = tile_keys(q0, q_last, stair);
 
   WgPlan p;
   p.q = a.q + (size_t)base * a.hq * D + (size_t)head * D;
@@ -418,9 +419,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd_pp_kernel(FwdArgs a, int nt
   p.r1e = tk.r1e;
   p.r2s = tk.r2s;
   p.r2e = tk.r2e;
-  p.P = P;
-  p.L = L;
-  p.B = a.block_size;
+  p.stair = stair;
   p.qw0 = q0 + (wave / a.hpw) * kRows;
 
   WaveState<D> ws;

@@ -33,9 +33,8 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdF32Args a) {
   const int ntiles = (L + kF32Rows - 1) / kF32Rows;
   if (rank >= ntiles) return;
   const int tile = ntiles - 1 - rank;
-  const int S = a.s_copies ? a.s_copies[seg] : 0;
-  int P = L - S * a.block_size;
-  if (P < 0) P = 0;
+  const Stair stair = make_stair(seg, L, a.block_size, a.s_copies, a.group_start, a.group_pe,
+                                 a.group_copies);
   const int g = head / (a.hq / a.hkv);
 
   const int tid = threadIdx.x;
@@ -44,8 +43,8 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdF32Args a) {
   const int qi = q0 + (tid >> 1);
   const bool valid = qi < L;
   const int q_last = min(q0 + kF32Rows, L) - 1;
-  const TileKeys tk = tile_keys(q0, q_last, P, L, a.block_size);
-  const RowKeys rk = row_keys(valid ? qi : q_last, P, L, a.block_size);
+  const TileKeys tk = tile_keys(q0, q_last, stair);
+  const RowKeys rk = row_keys(valid ? qi : q_last, stair);
 
   float qv[DH];
   const float* qrow = a.q + ((size_t)(base + (valid ? qi : q_last)) * a.hq + head) * D + half * DH;

@@ -75,12 +75,16 @@ const char* bca_status_string(int32_t status) {
 
 const char* bca_last_error(void) { return g_last_error; }
 
-bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                               const int32_t* cu_seqlens, const int32_t* s_copies, int32_t nseq,
-                               int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
-                               int32_t d, int32_t block_size, float scale, bca_dtype_t dtype,
-                               void* stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+// Forward of every packed variant: per-segment copies (s_copies) or a table of
+// copy groups (group_start / group_pe / group_copies), or neither.
+static bca_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens, const int32_t* s_copies,
+                             const int32_t* group_start, const int32_t* group_pe,
+                             const int32_t* group_copies, int32_t nseq, int32_t max_seqlen,
+                             int32_t total, int32_t hq, int32_t hkv, int32_t d,
+                             int32_t block_size, float scale, bca_dtype_t dtype, void* stream) {
   bca_status_t st = check_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total, hq, hkv,
                                  d, block_size, scale);
   if (st != BCA_OK) return st;
@@ -98,6 +102,9 @@ bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void
     a.lse = lse;
     a.cu_seqlens = cu_seqlens;
     a.s_copies = s_copies;
+    a.group_start = group_start;
+    a.group_pe = group_pe;
+    a.group_copies = group_copies;
     a.nseq = nseq;
     a.total = total;
     a.hq = hq;
@@ -116,6 +123,9 @@ bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void
   a.lse = lse;
   a.cu_seqlens = cu_seqlens;
   a.s_copies = s_copies;
+  a.group_start = group_start;
+  a.group_pe = group_pe;
+  a.group_copies = group_copies;
   a.nseq = nseq;
   a.total = total;
   a.hq = hq;
@@ -124,6 +134,32 @@ bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void
   a.block_size = block_size;
   a.scale_log2 = scale * kLog2e;
   return hip_status(bca::launch_fwd_f32(a, max_seqlen, s), "forward launch");
+}
+
+extern "C" {
+
+bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens, const int32_t* s_copies, int32_t nseq,
+                               int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                               int32_t d, int32_t block_size, float scale, bca_dtype_t dtype,
+                               void* stream) {
+  g_last_error[0] = '\0';
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, s_copies, nullptr, nullptr, nullptr, nseq,
+                  max_seqlen, total, hq, hkv, d, block_size, scale, dtype, stream);
+}
+
+bca_status_t bca_staircase_groups_fwd(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, const int32_t* cu_seqlens,
+                                      const int32_t* group_start, const int32_t* group_pe,
+                                      const int32_t* group_copies, int32_t nseq,
+                                      int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                                      int32_t d, int32_t block_size, float scale,
+                                      bca_dtype_t dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (nseq > 0 && total > 0 && (!group_start || !group_pe || !group_copies))
+    return fail(BCA_ERR_NULL, "group_start, group_pe and group_copies are required");
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, nullptr, group_start, group_pe, group_copies,
+                  nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype, stream);
 }
 
 bca_status_t bca_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -140,13 +176,16 @@ size_t bca_staircase_bwd_workspace(int32_t total, int32_t hq, int32_t hkv, int32
   return (delta + 255) & ~(size_t)255;
 }
 
-bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, const void* o,
-                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                               const int32_t* cu_seqlens, const int32_t* s_copies, int32_t nseq,
-                               int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
-                               int32_t d, int32_t block_size, float scale, bca_dtype_t dtype,
-                               void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error[0] = '\0';
+}  // extern "C"
+
+static bca_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens, const int32_t* s_copies,
+                             const int32_t* group_start, const int32_t* group_pe,
+                             const int32_t* group_copies, int32_t nseq, int32_t max_seqlen,
+                             int32_t total, int32_t hq, int32_t hkv, int32_t d,
+                             int32_t block_size, float scale, bca_dtype_t dtype, void* workspace,
+                             size_t ws_bytes, void* stream) {
   bca_status_t st = check_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total, hq, hkv,
                                  d, block_size, scale);
   if (st != BCA_OK) return st;
@@ -173,6 +212,9 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
   a.delta = static_cast<float*>(workspace);
   a.cu_seqlens = cu_seqlens;
   a.s_copies = s_copies;
+  a.group_start = group_start;
+  a.group_pe = group_pe;
+  a.group_copies = group_copies;
   a.nseq = nseq;
   a.total = total;
   a.hq = hq;
@@ -183,6 +225,37 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
   a.scale_log2 = scale * kLog2e;
   return hip_status(bca::launch_bwd_bf16(a, max_seqlen, static_cast<hipStream_t>(stream)),
                     "backward launch");
+}
+
+extern "C" {
+
+bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               const int32_t* cu_seqlens, const int32_t* s_copies, int32_t nseq,
+                               int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                               int32_t d, int32_t block_size, float scale, bca_dtype_t dtype,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, s_copies, nullptr, nullptr,
+                  nullptr, nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype,
+                  workspace, ws_bytes, stream);
+}
+
+bca_status_t bca_staircase_groups_bwd(const void* q, const void* k, const void* v,
+                                      const void* o, const float* lse, const void* dout,
+                                      void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                                      const int32_t* group_start, const int32_t* group_pe,
+                                      const int32_t* group_copies, int32_t nseq,
+                                      int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                                      int32_t d, int32_t block_size, float scale,
+                                      bca_dtype_t dtype, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  g_last_error[0] = '\0';
+  if (nseq > 0 && total > 0 && (!group_start || !group_pe || !group_copies))
+    return fail(BCA_ERR_NULL, "group_start, group_pe and group_copies are required");
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nullptr, group_start, group_pe,
+                  group_copies, nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype,
+                  workspace, ws_bytes, stream);
 }
 
 // Split-KV plan of the decode step: the 64-key tiles are dealt evenly to

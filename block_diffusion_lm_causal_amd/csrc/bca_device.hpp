@@ -95,33 +95,95 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Admitted keys of one query row.
 //
 // Block-causal attention ("On-Policy Residual Learning for Diffusion Language
-// Models", thread page, highlight 3) and its staircase packed-replay variant
-// (paper cards page, Figure 3 caption): in a segment of L tokens whose last
-// S*B tokens are S copies of one B-token block and whose first P = L - S*B
-// tokens are the clean prefix,
-//   prefix row i < P   : keys [0, min(P, (floor(i/B) + 1) * B))
-//   copy row, copy c   : keys [0, P)  and  [P + c*B, P + (c+1)*B)
-// Positions are relative to the segment start.  With S = 0, P = L and the
-// last (possibly partial) block stays bidirectional.
+// Models", thread page, highlight 3) and its staircase packed-replay variants
+// (paper cards page, Figure 3 caption; thread page, Insight 3).  A segment of
+// L tokens is a clean prefix of P tokens followed by copies of B-token blocks,
+// grouped: the copies of group g are noisy states of one block and see the
+// clean keys [0, pe_g) (pe_g = that block's start; groups ordered by pe_g,
+// non-decreasing) and, bidirectionally, their own B tokens.  The plain
+// staircase is one group with pe = P; plain block-causal has no copies.
+//   prefix row i < P       : keys [0, min(P, (floor(i/B) + 1) * B))
+//   copy row of copy c     : keys [0, pe_g(c))  and  [P + c*B, P + (c+1)*B)
+// Positions are relative to the segment start; copies are numbered from 0
+// over the whole segment.  With no copies, P = L and the last (possibly
+// partial) block stays bidirectional.
+struct Stair {
+  int P, L, B;
+  int S;                   // copies in the segment
+  const int32_t* gpe;      // group prefix ends (NULL: one group with pe = P)
+  const int32_t* gcp;      // copies per group
+  int ng;                  // groups
+};
+
+// The segment's rule from the packed metadata: per-segment copy counts
+// (s_copies, one group with pe = P) or a group table (group_start [nseq+1]
+// indexing group_pe / group_copies).
+__device__ __forceinline__ Stair make_stair(int seg, int L, int B, const int32_t* s_copies,
+                                            const int32_t* group_start, const int32_t* group_pe,
+                                            const int32_t* group_copies) {
+  Stair st;
+  st.L = L;
+  st.B = B;
+  st.gpe = nullptr;
+  st.gcp = nullptr;
+  st.ng = 0;
+  int S = 0;
+  if (group_start) {
+    const int g0 = group_start[seg], g1 = group_start[seg + 1];
+    st.gpe = group_pe + g0;
+    st.gcp = group_copies + g0;
+    st.ng = g1 - g0;
+    for (int g = 0; g < st.ng; ++g) S += st.gcp[g];
+  } else if (s_copies) {
+    S = s_copies[seg];
+  }
+  st.S = S;
+  const int P = L - S * B;
+  st.P = P < 0 ? 0 : P;
+  return st;
+}
+
+// Clean keys seen by copy c: the prefix end of its group.
+__device__ __forceinline__ int copy_prefix_end(const Stair& st, int c) {
+  if (!st.gpe) return st.P;
+  int acc = 0;
+  for (int g = 0; g < st.ng; ++g) {
+    acc += st.gcp[g];
+    if (c < acc) return st.gpe[g];
+  }
+  return st.P;
+}
+
+// First copy whose group sees clean key j (j < P); S if none does.
+__device__ __forceinline__ int first_copy_seeing(const Stair& st, int j) {
+  if (!st.gpe) return 0;
+  int acc = 0;
+  for (int g = 0; g < st.ng; ++g) {
+    if (st.gpe[g] > j) return acc;
+    acc += st.gcp[g];
+  }
+  return acc;
+}
+
 struct RowKeys {
   int e1;  // first interval is [0, e1)
   int s2;  // second interval is [s2, e2) (empty for prefix rows)
   int e2;
 };
 
-__device__ __forceinline__ RowKeys row_keys(int i, int P, int L, int B) {
+__device__ __forceinline__ RowKeys row_keys(int i, const Stair& st) {
   RowKeys r;
-  if (i < P) {
-    int e = (i / B + 1) * B;
-    r.e1 = e < P ? e : P;
+  if (i < st.P) {
+    int e = (i / st.B + 1) * st.B;
+    r.e1 = e < st.P ? e : st.P;
     r.s2 = 0;
     r.e2 = 0;
   } else {
-    int c = (i - P) / B;
-    int e = P + (c + 1) * B;
-    r.e1 = P;
-    r.s2 = P + c * B;
-    r.e2 = e < L ? e : L;
+    int c = (i - st.P) / st.B;
+    int e = st.P + (c + 1) * st.B;
+    r.e1 = copy_prefix_end(st, c);
+    r.s2 = st.P + c * st.B;
+    r.e2 = e < st.L ? e : st.L;
   }
   return r;
 }
@@ -130,26 +192,39 @@ __device__ __forceinline__ bool admitted(const RowKeys& r, int j) {
   return j < r.e1 || (j >= r.s2 && j < r.e2);
 }
 
-// The query rows that admit key j (0 <= j < L), which always form one
-// interval [lo, hi): a prefix key of block floor(j/B) is seen by the prefix
-// rows of that block and later ones and by every copy row; a key of copy c
-// only by the rows of copy c.
+// The query rows that admit key j (0 <= j < L): at most two intervals.  A
+// clean key of block floor(j/B) is seen by the prefix rows of that block and
+// later ones, [lo, P), and by the copies of every group with pe > j -- with
+// groups ordered by pe, a final run of copies [c_lo, L); a key of copy c only
+// by the rows of copy c.
 struct KeyRows {
-  int lo, hi;
+  int lo, hi;    // first interval
+  int lo2, hi2;  // second interval (empty if lo2 >= hi2)
 };
 
-__device__ __forceinline__ KeyRows key_rows(int j, int P, int L, int B) {
+__device__ __forceinline__ KeyRows key_rows(int j, const Stair& st) {
   KeyRows r;
-  if (j < P) {
-    r.lo = (j / B) * B;
-    r.hi = L;
+  if (j < st.P) {
+    r.lo = (j / st.B) * st.B;
+    r.hi = st.P;
+    r.lo2 = st.P + first_copy_seeing(st, j) * st.B;
+    r.hi2 = st.L;
+    if (r.lo2 == r.hi) {  // every copy sees the key: one interval
+      r.hi = st.L;
+      r.lo2 = r.hi2 = 0;
+    }
   } else {
-    const int c = (j - P) / B;
-    const int e = P + (c + 1) * B;
-    r.lo = P + c * B;
-    r.hi = e < L ? e : L;
+    const int c = (j - st.P) / st.B;
+    const int e = st.P + (c + 1) * st.B;
+    r.lo = st.P + c * st.B;
+    r.hi = e < st.L ? e : st.L;
+    r.lo2 = r.hi2 = 0;
   }
   return r;
+}
+
+__device__ __forceinline__ bool row_sees(const KeyRows& r, int i) {
+  return (i >= r.lo && i < r.hi) || (i >= r.lo2 && i < r.hi2);
 }
 
 // Key ranges a tile of query rows [q_first, q_last] (inclusive, all inside
@@ -160,25 +235,42 @@ struct TileKeys {
   int r2e;
 };
 
-__device__ __forceinline__ TileKeys tile_keys(int q_first, int q_last, int P, int L, int B) {
+__device__ __forceinline__ TileKeys tile_keys(int q_first, int q_last, const Stair& st) {
   TileKeys t;
+  const int P = st.P, B = st.B;
   if (q_last < P) {
     int e = (q_last / B + 1) * B;
     t.r1e = e < P ? e : P;
     t.r2s = t.r2e = 0;
   } else {
-    int c_first = q_first >= P ? (q_first - P) / B : 0;
-    int c_last = (q_last - P) / B;
-    t.r1e = P;
+    const int c_first = q_first >= P ? (q_first - P) / B : 0;
+    const int c_last = (q_last - P) / B;
+    // clean keys: the largest prefix end among the tile's rows (prefix ends
+    // grow with the copy index; prefix rows reach at most P)
+    int e1 = copy_prefix_end(st, c_last);
+    if (q_first < P) e1 = P;
+    t.r1e = e1;
     t.r2s = P + c_first * B;
     t.r2e = P + (c_last + 1) * B;
-    if (t.r2e > L) t.r2e = L;
+    if (t.r2e > st.L) t.r2e = st.L;
   }
   if (t.r2e > t.r2s && t.r2s <= t.r1e) {  // contiguous: one range
     t.r1e = t.r2e > t.r1e ? t.r2e : t.r1e;
     t.r2s = t.r2e = 0;
   }
   return t;
+}
+
+// Smallest clean-key end among rows [q_first, q_last]: prefix ends grow along
+// the prefix and along the copies, so it is the first row's or the first copy
+// row's.
+__device__ __forceinline__ int min_prefix_end(int q_first, int q_last, const Stair& st) {
+  int e = row_keys(q_first, st).e1;
+  if (q_first < st.P && q_last >= st.P) {
+    const int e2 = row_keys(st.P, st).e1;
+    e = e2 < e ? e2 : e;
+  }
+  return e;
 }
 
 }  // namespace bca

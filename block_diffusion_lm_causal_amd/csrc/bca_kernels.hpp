@@ -15,7 +15,10 @@ struct FwdArgs {
   uint16_t* o;        // [total, hq, d]
   float* lse;         // [hq, total]
   const int32_t* cu_seqlens;
-  const int32_t* s_copies;  // may be NULL
+  const int32_t* s_copies;      // may be NULL
+  const int32_t* group_start;   // copy groups (NULL: s_copies rule), [nseq + 1]
+  const int32_t* group_pe;      // prefix end per group
+  const int32_t* group_copies;  // copies per group
   int nseq, total, hq, hkv, d, block_size;
   int hpw;            // query heads per workgroup (4, 2 or 1; divides hq / hkv)
   float scale_log2;   // scale * log2(e)
@@ -29,6 +32,9 @@ struct FwdF32Args {
   float* lse;
   const int32_t* cu_seqlens;
   const int32_t* s_copies;
+  const int32_t* group_start;
+  const int32_t* group_pe;
+  const int32_t* group_copies;
   int nseq, total, hq, hkv, d, block_size;
   float scale_log2;
 };
@@ -62,6 +68,9 @@ struct BwdArgs {
   float* delta;       // [hq, total] float32 workspace: rowsum(dO * O)
   const int32_t* cu_seqlens;
   const int32_t* s_copies;
+  const int32_t* group_start;
+  const int32_t* group_pe;
+  const int32_t* group_copies;
   int nseq, total, hq, hkv, d, block_size;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)

@@ -36,7 +36,7 @@ class Workload:
     """
 
     name: str
-    kind: str                 # "fwd", "staircase_fwd", "staircase_bwd", "decode"
+    kind: str                 # "fwd", "staircase_fwd", "staircase_bwd", "decode", "staircase_groups"
     dtype: str                # "f32" or "bf16"
     hq: int
     hkv: int
@@ -51,6 +51,8 @@ class Workload:
     do: Optional[torch.Tensor] = None
     prefix_lens: Optional[np.ndarray] = None
     seed: int = 0
+    # general staircase: per segment a list of (prefix end, copies) groups
+    groups: Optional[list] = None
 
     @property
     def total(self) -> int:
@@ -63,6 +65,16 @@ class Workload:
     @property
     def max_seqlen(self) -> int:
         return int(np.max(np.diff(self.cu_seqlens))) if self.nseq else 0
+
+    def group_table(self):
+        """(group_start [nseq+1], group_pe [G], group_copies [G]) int32 arrays."""
+        if self.groups is None:
+            raise ValueError("not a general staircase workload")
+        start = np.zeros(self.nseq + 1, dtype=np.int32)
+        start[1:] = np.cumsum([len(g) for g in self.groups])
+        pe = np.array([p for g in self.groups for p, _ in g], dtype=np.int32)
+        cp = np.array([c for g in self.groups for _, c in g], dtype=np.int32)
+        return start, pe, cp
 
     def describe(self) -> dict:
         return {
@@ -170,6 +182,37 @@ def staircase_bwd_16traj() -> Workload:
     prefix, copies, seqlens = staircase_lengths(rng, 16, 64, 16, 128, 4, 24)
     return packed("staircase_fwdbwd_bf16_16traj_B64", "staircase_bwd", 4, seqlens, copies,
                   32, 8, 128, 64, "bf16", with_do=True, rng=rng, prefix_lens=prefix)
+
+
+def general_staircase(name: str, seed: int, ntraj: int, block_size: int, blocks_lo: int,
+                      blocks_hi: int, copies_lo: int, copies_hi: int, hq: int, hkv: int, d: int,
+                      dtype: str, with_do: bool = False) -> Workload:
+    """Trajectories replayed with a copy group per block.
+
+    Each trajectory has n = U{blocks_lo..blocks_hi} clean blocks (P = n B
+    tokens); block b gets U{copies_lo..copies_hi} copies, each seeing the
+    clean keys before block b ([0, b B)) and itself.  Draw order: all block
+    counts, then the copy counts trajectory by trajectory, block by block,
+    then Q, K, V (and dO).
+    """
+    rng = np.random.default_rng(seed)
+    nblocks = rng.integers(blocks_lo, blocks_hi + 1, size=ntraj)
+    groups, seqlens, copies = [], [], []
+    for n in nblocks.tolist():
+        cps = rng.integers(copies_lo, copies_hi + 1, size=n).tolist()
+        groups.append([(b * block_size, int(c)) for b, c in enumerate(cps)])
+        copies.append(int(sum(cps)))
+        seqlens.append(n * block_size + int(sum(cps)) * block_size)
+    w = packed(name, "staircase_groups", seed, seqlens, copies, hq, hkv, d, block_size, dtype,
+               with_do=with_do, rng=rng, prefix_lens=nblocks * block_size)
+    w.groups = groups
+    return w
+
+
+def staircase_groups_8traj() -> Workload:
+    """8 trajectories, 8-32 clean blocks of 32 tokens, 1-4 copies per block, dO, seed 6."""
+    return general_staircase("staircase_groups_bf16_8traj_B32", 6, 8, 32, 8, 32, 1, 4, 32, 8,
+                             128, "bf16", with_do=True)
 
 
 def useful_pairs(seqlens, s_copies, block_size: int) -> int:

@@ -140,6 +140,43 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
                                bca_dtype_t dtype, void* workspace, size_t ws_bytes,
                                void* stream);
 
+/*
+ * General trajectory staircase (paper cards page, Figure 3 caption; thread
+ * page, Insight 3: a trajectory's captured denoising states are replayed
+ * together).  A segment is a clean prefix of P tokens followed by groups of
+ * block copies; the copies of group g are noisy states of one block and see
+ * the clean keys [0, pe_g) -- the tokens before that block -- and,
+ * bidirectionally, their own B tokens; clean rows stay block-causal.
+ *   group_start  : device int32 [nseq + 1]; segment s owns groups
+ *                  [group_start[s], group_start[s+1])
+ *   group_pe     : device int32 [groups], prefix end pe_g of each group
+ *                  (a multiple of B, 0 <= pe_g <= P, non-decreasing within a
+ *                  segment)
+ *   group_copies : device int32 [groups], copies of each group (>= 0)
+ * Group g's copies follow group g-1's, and P = L - B * (sum of the segment's
+ * copies) must be >= 0 and a multiple of B when there are copies.  A segment
+ * with one group whose pe is P is the plain staircase.  Other arguments,
+ * layouts and errors as bca_staircase_fwd / bca_staircase_bwd (the table
+ * contents, like cu_seqlens, are the caller's contract).
+ */
+bca_status_t bca_staircase_groups_fwd(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, const int32_t* cu_seqlens,
+                                      const int32_t* group_start, const int32_t* group_pe,
+                                      const int32_t* group_copies, int32_t nseq,
+                                      int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                                      int32_t d, int32_t block_size, float scale,
+                                      bca_dtype_t dtype, void* stream);
+
+bca_status_t bca_staircase_groups_bwd(const void* q, const void* k, const void* v,
+                                      const void* o, const float* lse, const void* dout,
+                                      void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                                      const int32_t* group_start, const int32_t* group_pe,
+                                      const int32_t* group_copies, int32_t nseq,
+                                      int32_t max_seqlen, int32_t total, int32_t hq, int32_t hkv,
+                                      int32_t d, int32_t block_size, float scale,
+                                      bca_dtype_t dtype, void* workspace, size_t ws_bytes,
+                                      void* stream);
+
 /* Bytes of workspace bca_decode needs for `num_splits` key chunks
  * (num_splits = 0: the count bca_decode would choose itself).  Returns 0 for
  * invalid sizes. */

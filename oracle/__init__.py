@@ -11,9 +11,10 @@ for the block_size = 1 (causal) and block_size = L (full) special cases, a
 hand-derived table of admitted keys, closed forms at Q = 0, finite differences
 and torch autograd for the gradients, and the invariants of softmax attention.
 """
-from .attention import (allowed_matrix, attention_bwd, attention_dq_rows, attention_fwd,
-                        decode, segment_prefix_len)
+from .attention import (allowed_matrix, allowed_matrix_groups, attention_bwd,
+                        attention_dq_rows, attention_fwd, decode, segment_allowed,
+                        segment_prefix_len)
 from .packing import lpt, optimal_makespan, trajectory_cost
 
-__all__ = ["allowed_matrix", "attention_bwd", "attention_dq_rows", "attention_fwd", "decode",
+__all__ = ["allowed_matrix", "allowed_matrix_groups", "segment_allowed", "attention_bwd", "attention_dq_rows", "attention_fwd", "decode",
            "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost"]

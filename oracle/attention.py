@@ -73,6 +73,51 @@ def allowed_matrix(seqlen: int, copies: int, block_size: int) -> np.ndarray:
     return np.where(i < P, prefix_rows, copy_rows)
 
 
+def allowed_matrix_groups(seqlen: int, groups, block_size: int) -> np.ndarray:
+    """allowed[i, j] for a general trajectory staircase segment.
+
+    ``groups`` lists (pe, copies) in segment order: after the clean prefix of
+    P = L - B * (total copies) tokens come the copies of group 0, then of
+    group 1, ...; a copy of group g is a noisy state of the block starting at
+    clean position pe and sees the clean keys [0, pe) plus, bidirectionally,
+    its own B tokens.  Clean rows are block-causal inside the prefix.  Every
+    pe must be a multiple of B in [0, P], non-decreasing along the segment.
+    """
+    B = block_size
+    total_copies = sum(int(c) for _, c in groups)
+    P = segment_prefix_len(seqlen, total_copies, B)
+    prev = 0
+    for pe, c in groups:
+        if c < 0 or pe % B != 0 or not (0 <= pe <= P) or pe < prev:
+            raise ValueError(f"bad copy group (pe={pe}, copies={c}) for P={P}, B={B}")
+        prev = pe
+    i = np.arange(seqlen)[:, None]
+    j = np.arange(seqlen)[None, :]
+    allowed = (i < P) & (j < P) & ((j // B) <= (i // B))
+    row = P
+    for pe, c in groups:
+        for _ in range(int(c)):
+            own = slice(row, row + B)
+            allowed[own, :pe] = True
+            allowed[own, own] = True
+            row += B
+    return allowed
+
+
+def segment_allowed(seqlen: int, spec, block_size: int) -> np.ndarray:
+    """Admitted-key matrix of one segment: ``spec`` is a copy count S (one
+    group seeing the whole prefix) or a list of (pe, copies) groups."""
+    if isinstance(spec, (list, tuple)):
+        return allowed_matrix_groups(seqlen, spec, block_size)
+    return allowed_matrix(seqlen, int(spec), block_size)
+
+
+def _segment_specs(s_copies, nseq: int):
+    if s_copies is None:
+        return [0] * nseq
+    return [x if isinstance(x, (list, tuple)) else int(x) for x in s_copies]
+
+
 def _kv_head(h: int, hq: int, hkv: int) -> int:
     if hq % hkv != 0:
         raise ValueError("query heads must be a multiple of KV heads")
@@ -93,7 +138,7 @@ def attention_fwd(q, k, v, cu_seqlens, s_copies, block_size: int, scale: float,
     hkv = k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     nseq = len(cu) - 1
-    sc = np.zeros(nseq, np.int64) if s_copies is None else np.asarray(s_copies, np.int64)
+    sc = _segment_specs(s_copies, nseq)
     heads = range(hq) if heads is None else heads
     want = np.ones(total, bool) if rows is None else np.isin(np.arange(total), rows)
 
@@ -104,7 +149,7 @@ def attention_fwd(q, k, v, cu_seqlens, s_copies, block_size: int, scale: float,
         L = b - a
         if L == 0:
             continue
-        allowed = allowed_matrix(L, int(sc[s]), block_size)
+        allowed = segment_allowed(L, sc[s], block_size)
         local_rows = np.nonzero(want[a:b])[0]
         for h in heads:
             g = _kv_head(h, hq, hkv)
@@ -136,7 +181,7 @@ def attention_bwd(q, k, v, do, cu_seqlens, s_copies, block_size: int, scale: flo
     hkv = k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     nseq = len(cu) - 1
-    sc = np.zeros(nseq, np.int64) if s_copies is None else np.asarray(s_copies, np.int64)
+    sc = _segment_specs(s_copies, nseq)
 
     O = np.zeros((total, hq, d))
     LSE = np.zeros((hq, total))
@@ -148,7 +193,7 @@ def attention_bwd(q, k, v, do, cu_seqlens, s_copies, block_size: int, scale: flo
         L = b - a
         if L == 0:
             continue
-        allowed = allowed_matrix(L, int(sc[s]), block_size)
+        allowed = segment_allowed(L, sc[s], block_size)
         for h in range(hq):
             g = _kv_head(h, hq, hkv)
             K = k[a:b, g, :]
@@ -208,7 +253,7 @@ def attention_dq_rows(q, k, v, do, cu_seqlens, s_copies, block_size: int, scale:
     hkv = k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     nseq = len(cu) - 1
-    sc = np.zeros(nseq, np.int64) if s_copies is None else np.asarray(s_copies, np.int64)
+    sc = _segment_specs(s_copies, nseq)
     heads = range(hq) if heads is None else heads
     rows = np.asarray(rows, dtype=np.int64)
     dQ = np.full((total, hq, d), np.nan)
@@ -217,7 +262,7 @@ def attention_dq_rows(q, k, v, do, cu_seqlens, s_copies, block_size: int, scale:
         r = rows[(rows >= a) & (rows < b)] - a
         if len(r) == 0:
             continue
-        allowed = allowed_matrix(b - a, int(sc[s]), block_size)[r]
+        allowed = segment_allowed(b - a, sc[s], block_size)[r]
         for h in heads:
             g = _kv_head(h, hq, hkv)
             K = k[a:b, g, :]

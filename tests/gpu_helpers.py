@@ -37,6 +37,25 @@ def run_fwd(w: Workload, staircase: bool = True):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
+def segment_spec(w: Workload, s: int):
+    """The oracle's copy description of segment s: its copy groups, or S."""
+    return w.groups[s] if w.groups is not None else int(w.s_copies[s])
+
+
+def group_tensors(w: Workload):
+    dev = torch.device("cuda", 0)
+    return tuple(torch.from_numpy(x).to(dev) for x in w.group_table())
+
+
+def run_groups_fwd(w: Workload):
+    q, k, v, cu, _, _ = device_inputs(w)
+    gs, gp, gc = group_tensors(w)
+    o, lse = bca.staircase_groups_fwd(q, k, v, cu, gs, gp, gc, w.block_size, w.scale,
+                                      w.max_seqlen)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
 def oracle_rows(w: Workload, rows, heads=None):
     """Oracle O/LSE on selected global rows, one segment at a time."""
     rows = np.unique(np.asarray(rows, np.int64))
@@ -49,7 +68,7 @@ def oracle_rows(w: Workload, rows, heads=None):
         if len(r) == 0:
             continue
         o, lse = oracle.attention_fwd(w.q[a:b], w.k[a:b], w.v[a:b], [0, b - a],
-                                      [int(w.s_copies[s])], w.block_size, w.scale,
+                                      [segment_spec(w, s)], w.block_size, w.scale,
                                       heads=heads, rows=r - a)
         O[a:b][r - a] = o[r - a]
         LSE[:, a:b][:, r - a] = lse[:, r - a]
@@ -70,6 +89,12 @@ def sample_rows(w: Workload, rng: np.random.Generator, per_segment: int = 6):
         P = L - int(w.s_copies[s]) * B
         cand = [0, L - 1, min(L - 1, B - 1), min(L - 1, B), P - 1, P, P + B - 1, P + B,
                 min(L - 1, 31), min(L - 1, 32), min(L - 1, 127), min(L - 1, 128)]
+        if w.groups is not None:  # first and last row of every copy group
+            row = P
+            for _, c in w.groups[s]:
+                if c:
+                    cand += [row, row + c * B - 1]
+                row += c * B
         cand += rng.integers(0, L, size=per_segment).tolist()
         rows += [a + c for c in cand if 0 <= c < L]
     return np.unique(rows)

@@ -377,3 +377,103 @@ def test_useful_pair_count_matches_mask():
     from block_diffusion_lm_causal_amd.workloads import useful_pairs
     for L, S, B in [(256, 0, 32), (7, 0, 3), (10, 3, 2), (104, 5, 8), (37, 0, 5), (40, 5, 8), (64, 0, 1)]:
         assert useful_pairs([L], [S], B) == int(oracle.allowed_matrix(L, S, B).sum())
+
+
+# --------------------------------------------------------------------------- copy groups
+
+def test_groups_admitted_keys_match_hand_table():
+    table = read_golden("staircase_groups_allowed_L12_P6_B2.txt")
+    L, B, groups = 12, 2, [(2, 1), (4, 2)]
+    q = np.zeros((L, 1, L))
+    k = np.random.default_rng(1).standard_normal((L, 1, L))
+    v = np.eye(L)[:, None, :]
+    o, lse = oracle.attention_fwd(q, k, v, [0, L], [groups], B, 1.0)
+    for i in range(L):
+        keys = table[i]
+        expect = np.zeros(L)
+        expect[keys] = 1.0 / len(keys)
+        np.testing.assert_allclose(o[i, 0], expect, rtol=0, atol=1e-15)
+        assert abs(lse[0, i] - math.log(len(keys))) < 1e-14
+    allowed = oracle.allowed_matrix_groups(L, groups, B)
+    for i in range(L):
+        assert sorted(np.nonzero(allowed[i])[0].tolist()) == table[i]
+
+
+@pytest.mark.parametrize("L,S,B", [(10, 3, 2), (40, 2, 8), (9, 0, 3)])
+def test_one_group_seeing_the_whole_prefix_is_the_staircase(L, S, B):
+    P = L - S * B
+    groups = [(P, S)] if S else []
+    assert np.array_equal(oracle.allowed_matrix_groups(L, groups, B),
+                          oracle.allowed_matrix(L, S, B))
+
+
+def test_copy_equal_to_its_clean_block_reproduces_block_causal_rows():
+    # A copy whose Q/K/V equal clean block b sees exactly what clean block b
+    # sees in block-causal attention over the clean sequence, so its rows of
+    # O and LSE equal those of block b.
+    rng = np.random.default_rng(21)
+    B, nb, hq, hkv, d = 4, 5, 4, 2, 8
+    P = nb * B
+    cq, ck, cv = rnd(rng, P, hq, d), rnd(rng, P, hkv, d), rnd(rng, P, hkv, d)
+    o_clean, lse_clean = oracle.attention_fwd(cq, ck, cv, [0, P], None, B, 0.3)
+    blocks = [0, 2, 2, 4]          # one copy of block 0, two of block 2, one of block 4
+    groups = [(0, 1), (2 * B, 2), (4 * B, 1)]
+    rows = np.concatenate([np.arange(P)] + [np.arange(b * B, (b + 1) * B) for b in blocks])
+    o, lse = oracle.attention_fwd(cq[rows], ck[rows], cv[rows], [0, len(rows)], [groups], B,
+                                  0.3)
+    np.testing.assert_allclose(o, o_clean[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_clean[:, rows], rtol=0, atol=1e-12)
+
+
+def test_group_rows_decompose_into_block_causal_pieces():
+    # With random copy values, a copy of the block at clean position pe gives
+    # the last-block rows of block-causal attention on [clean[0:pe] ++ copy].
+    rng = np.random.default_rng(22)
+    B, P, hq, hkv, d = 4, 16, 2, 1, 8
+    groups = [(0, 2), (8, 1), (16, 2)]
+    L = P + B * sum(c for _, c in groups)
+    q, k, v = rnd(rng, L, hq, d), rnd(rng, L, hkv, d), rnd(rng, L, hkv, d)
+    o, lse = oracle.attention_fwd(q, k, v, [0, L], [groups], B, 0.4)
+    row = P
+    for pe, c in groups:
+        for _ in range(c):
+            idx = np.concatenate([np.arange(pe), np.arange(row, row + B)])
+            o_p, lse_p = oracle.attention_fwd(q[idx], k[idx], v[idx], [0, len(idx)], None, B, 0.4)
+            np.testing.assert_allclose(o[row:row + B], o_p[pe:], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[:, row:row + B], lse_p[:, pe:], rtol=0, atol=1e-12)
+            row += B
+    o_c, _ = oracle.attention_fwd(q[:P], k[:P], v[:P], [0, P], None, B, 0.4)
+    np.testing.assert_allclose(o[:P], o_c, rtol=0, atol=1e-12)
+
+
+def test_group_gradients_match_finite_differences():
+    rng = np.random.default_rng(23)
+    B, P, hq, hkv, d = 2, 6, 2, 1, 3
+    groups = [(2, 1), (6, 1)]
+    L = P + B * 2
+    q, k, v, do = (rnd(rng, L, hq, d), rnd(rng, L, hkv, d), rnd(rng, L, hkv, d),
+                   rnd(rng, L, hq, d))
+    _, _, dQ, dK, dV = oracle.attention_bwd(q, k, v, do, [0, L], [groups], B, 0.7)
+
+    def f(q_, k_, v_):
+        o, _ = oracle.attention_fwd(q_, k_, v_, [0, L], [groups], B, 0.7)
+        return float(np.sum(o * do))
+    h = 1e-6
+    for x, g in ((q, dQ), (k, dK), (v, dV)):
+        for idx in [(0, 0, 0), (L - 1, x.shape[1] - 1, d - 1), (5, 0, 1), (7, 0, 2)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fd = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-7, (idx, fd, g[idx])
+
+
+def test_bad_groups_rejected():
+    with pytest.raises(ValueError):
+        oracle.allowed_matrix_groups(12, [(4, 2), (2, 1)], 2)    # pe decreasing
+    with pytest.raises(ValueError):
+        oracle.allowed_matrix_groups(12, [(3, 3)], 2)            # pe not a block start
+    with pytest.raises(ValueError):
+        oracle.allowed_matrix_groups(8, [(8, 1)], 2)             # pe beyond P = 6
