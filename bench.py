@@ -18,13 +18,15 @@ under ``"paths"``:
   * staircase forward, 8 packed trajectories (block 32);
   * staircase forward and backward, 16 packed trajectories (block 64),
     backward FLOPs counted as 10 * d per admitted pair per query head;
+  * the general trajectory staircase (a group of copies per block), forward
+    and backward, 8 trajectories (block 32);
   * compute-balanced packing of trajectories into bins (host routine).
 
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 headline workload (whole query heads until about 10 s have elapsed).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-       [--only-headline] [--paths decode,staircase,packing] [--copy-calibration]
+       [--only-headline] [--paths decode,staircase,groups,packing] [--copy-calibration]
 Prints exactly one JSON line on stdout.
 """
 from __future__ import annotations
@@ -210,6 +212,48 @@ def bench_staircase(workload_fn, steps: int, warmup: int, backward: bool):
     return res
 
 
+def bench_groups(steps: int, warmup: int):
+    """General trajectory staircase (a copy group per block), forward and backward."""
+    import numpy as np
+    import torch
+    from block_diffusion_lm_causal_amd import bca, workloads
+    w = workloads.staircase_groups_8traj()
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (t.to(dev) for t in (w.q, w.k, w.v, w.do))
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    gs, gp, gc = (torch.from_numpy(x).to(dev) for x in w.group_table())
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.total), dtype=torch.float32, device=dev)
+    pairs = workloads.useful_pairs_groups(np.diff(w.cu_seqlens), w.groups, w.block_size)
+
+    def fwd():
+        bca.staircase_groups_fwd(q, k, v, cu, gs, gp, gc, w.block_size, w.scale, w.max_seqlen,
+                                 out=o, lse=lse)
+
+    per_call, _ = timed_calls(fwd, steps, warmup)
+    fwd_ms = statistics.median(per_call)
+    ws = torch.empty(bca.staircase_bwd_workspace(w.total, w.hq, w.hkv, w.d), dtype=torch.uint8,
+                     device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fwd()
+
+    def bwd():
+        bca.staircase_groups_bwd(q, k, v, o, lse, do, cu, gs, gp, gc, w.block_size, w.scale,
+                                 w.max_seqlen, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    per_call, _ = timed_calls(bwd, steps, warmup)
+    bwd_ms = statistics.median(per_call)
+    fwd_flops, bwd_flops = 4.0 * w.d * pairs * w.hq, 10.0 * w.d * pairs * w.hq
+    return {"workload": w.name, "total_tokens": w.total, "groups": int(gp.numel()),
+            "useful_pairs_per_head": pairs,
+            "fwd_ms_median": round(fwd_ms, 4),
+            "fwd_TFLOPs": round(fwd_flops / fwd_ms / 1e9, 1),
+            "fwd_frac_mfma": round(fwd_flops / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms_median": round(bwd_ms, 4),
+            "bwd_TFLOPs_10d": round(bwd_flops / bwd_ms / 1e9, 1),
+            "bwd_frac_mfma_10d": round(bwd_flops / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
 def bench_packing():
     """Compute-balanced packing (host): balance of the 16-trajectory workload
     over 8 bins, and the time to pack 10,000 random trajectories."""
@@ -265,8 +309,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--only-headline", action="store_true", help="time the headline case only")
-    ap.add_argument("--paths", default="decode,staircase,packing",
-                    help="comma list of extra paths to time: decode, staircase, packing")
+    ap.add_argument("--paths", default="decode,staircase,groups,packing",
+                    help="comma list of extra paths to time: decode, staircase, groups, packing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (a known-size "
                          "kernel against which HBM byte counters are scaled)")
@@ -310,6 +354,9 @@ def main() -> int:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")
             paths[f"decode_P{P}"] = bench_decode(P)
+    if "groups" in extra:
+        log("[bench] general staircase (copy groups), forward + backward, 8 trajectories")
+        paths["staircase_groups_fwdbwd_8traj"] = bench_groups(10, 3)
     if "packing" in extra:
         paths["packing"] = bench_packing()
     if "staircase" in extra:

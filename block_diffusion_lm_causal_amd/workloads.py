@@ -231,3 +231,19 @@ def useful_pairs(seqlens, s_copies, block_size: int) -> int:
         total += B * B * n * (n + 1) // 2 + r * (n * B + r)
         total += S * B * (P + B)
     return int(total)
+
+
+def useful_pairs_groups(seqlens, groups, block_size: int) -> int:
+    """Admitted (query, key) pairs per query head of general staircase
+    segments, in closed form: the clean prefix of n whole blocks (plus r
+    tokens) as in useful_pairs, and each copy of a group with prefix end pe
+    admits B (pe + B) pairs.  A cost model for measurement only."""
+    total = 0
+    B = block_size
+    for L, g in zip(np.asarray(seqlens).tolist(), groups):
+        S = sum(c for _, c in g)
+        P = L - S * B
+        n, r = divmod(P, B)
+        total += B * B * n * (n + 1) // 2 + r * (n * B + r)
+        total += sum(c * B * (pe + B) for pe, c in g)
+    return int(total)

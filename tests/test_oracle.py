@@ -477,3 +477,11 @@ def test_bad_groups_rejected():
         oracle.allowed_matrix_groups(12, [(3, 3)], 2)            # pe not a block start
     with pytest.raises(ValueError):
         oracle.allowed_matrix_groups(8, [(8, 1)], 2)             # pe beyond P = 6
+
+
+def test_group_pair_count_matches_mask():
+    from block_diffusion_lm_causal_amd import workloads as W
+    w = W.general_staircase("count", 9, 5, 8, 2, 9, 0, 3, 2, 1, 8, "f32")
+    want = sum(int(oracle.segment_allowed(int(L), g, 8).sum())
+               for L, g in zip(np.diff(w.cu_seqlens), w.groups))
+    assert W.useful_pairs_groups(np.diff(w.cu_seqlens), w.groups, 8) == want
