@@ -14,7 +14,7 @@ under ``"paths"``:
     (K and V read once per KV head, Q read, O and LSE written), median over
     32 calls with L2 and the Infinity Cache flushed before each call, plus the
     warm back-to-back figure and the per-step time of a captured 32-step
-    graph (caches warm), labelled;
+    graph (caches warm), labelled; the same against an FP8 E4M3 cache;
   * staircase forward, 8 packed trajectories (block 32);
   * staircase forward and backward, 16 packed trajectories (block 64),
     backward FLOPs counted as 10 * d per admitted pair per query head;
@@ -166,6 +166,36 @@ def bench_decode(prefix: int, calls: int = 32):
         "GBps_graph_replay_l2_resident": round(algo_bytes / graph_us / 1e3, 1),
         "calls": calls,
     }
+
+
+def bench_decode_fp8(prefix: int, calls: int = 32):
+    """Decode step against an FP8 E4M3 cache: K/V bytes halve."""
+    import torch
+    from block_diffusion_lm_causal_amd import bca, workloads
+    w, k8, v8, ks, vs = workloads.decode_step_fp8(prefix)
+    dev = torch.device("cuda", 0)
+    q, k8, v8 = w.q.to(dev), k8.to(dev), v8.to(dev)
+    kv_len = prefix + w.block_size
+    ws = torch.empty(max(bca.decode_workspace(w.block_size, kv_len, w.hq, w.hkv, w.d), 16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.block_size), dtype=torch.float32, device=dev)
+    algo_bytes = (2 * kv_len * w.hkv * w.d + 2 * w.block_size * w.hq * w.d * 2
+                  + w.hq * w.block_size * 4)
+    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def step():
+        bca.decode_fp8(q, k8, v8, ks, vs, w.scale, workspace=ws, out=o, lse=lse)
+
+    cold, _ = timed_calls(step, calls, 3, flush=lambda: flush_buf.fill_(1.0))
+    warm, _ = timed_calls(step, calls, 3)
+    cold_us = statistics.median(cold) * 1e3
+    warm_us = statistics.median(warm) * 1e3
+    return {"workload": w.name, "bytes_per_call": algo_bytes,
+            "us_per_call_flushed_median": round(cold_us, 3),
+            "GBps_flushed": round(algo_bytes / cold_us / 1e3, 1),
+            "frac_hbm_flushed": round(algo_bytes / cold_us / 1e3 / PEAK_HBM_GBS, 4),
+            "us_per_call_warm_median": round(warm_us, 3), "calls": calls}
 
 
 def bench_staircase(workload_fn, steps: int, warmup: int, backward: bool):
@@ -354,6 +384,9 @@ def main() -> int:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")
             paths[f"decode_P{P}"] = bench_decode(P)
+        for P in (1024, 8192):
+            log(f"[bench] decode, FP8 cache, P={P}")
+            paths[f"decode_fp8_P{P}"] = bench_decode_fp8(P)
     if "groups" in extra:
         log("[bench] general staircase (copy groups), forward + backward, 8 trajectories")
         paths["staircase_groups_fwdbwd_8traj"] = bench_groups(10, 3)

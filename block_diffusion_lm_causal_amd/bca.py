@@ -27,7 +27,7 @@ EXPORTS = (
     "bca_staircase_bwd_workspace", "bca_staircase_bwd", "bca_decode_workspace", "bca_decode",
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
-    "bca_staircase_groups_fwd", "bca_staircase_groups_bwd",
+    "bca_staircase_groups_fwd", "bca_staircase_groups_bwd", "bca_decode_fp8",
 )
 
 
@@ -90,6 +90,9 @@ def lib() -> ctypes.CDLL:
     L.bca_staircase_groups_bwd.restype = _I
     L.bca_staircase_groups_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]
+    L.bca_decode_fp8.restype = _I
+    L.bca_decode_fp8.argtypes = [_P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S,
+                                 _P]
     L.bca_trajectory_cost.restype = ctypes.c_int64
     L.bca_trajectory_cost.argtypes = [_I, _I, _I]
     L.bca_pack_balanced.restype = _I
@@ -335,6 +338,40 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
                           d, scale, _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
                           _stream(dev))
     _check("bca_decode", st)
+    return out, lse
+
+
+def decode_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: float,
+               v_scale: float, scale: Optional[float] = None, num_splits: int = 0,
+               workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode step against an FP8 E4M3 cache -> (O bf16 [q_len, hq, d], LSE [hq, q_len]).
+
+    k8/v8 are [kv_len, hkv, d] uint8 (or float8_e4m3fn) holding K / k_scale
+    and V / v_scale.
+    """
+    dev = _need_gpu(q, k8, v8, workspace, out, lse)
+    if k8.element_size() != 1 or v8.element_size() != 1:
+        raise BcaError("decode_fp8", 3, "k8 and v8 must hold one byte per element")
+    if q.dtype != torch.bfloat16:
+        raise BcaError("decode_fp8", 3, "q must be bfloat16")
+    q_len, hq, d = q.shape
+    kv_len, hkv = k8.shape[0], k8.shape[1]
+    if k8.shape != (kv_len, hkv, d) or v8.shape != k8.shape:
+        raise BcaError("decode_fp8", 2, "k8 and v8 must be [kv_len, hkv, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
+    st = lib().bca_decode_fp8(_ptr(q), _ptr(k8), _ptr(v8), float(k_scale), float(v_scale),
+                              _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv, d, scale,
+                              int(num_splits), _ptr(workspace), ws_bytes, _stream(dev))
+    _check("bca_decode_fp8", st)
     return out, lse
 
 

@@ -337,6 +337,9 @@ static bca_status_t decode_args(const void* q, const void* k, const void* v, voi
   a->hpw = bca::heads_per_wg(hq, hkv);
   a->nsplit = ns;
   a->scale_log2 = scale * kLog2e;
+  a->k8 = nullptr;
+  a->v8 = nullptr;
+  a->o_mul = 1.f;
   return BCA_OK;
 }
 
@@ -358,6 +361,26 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
                                       num_splits, workspace, ws_bytes, &a);
   if (st != BCA_OK) return st;
   return hip_status(bca::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float k_scale,
+                            float v_scale, void* o, float* lse, int32_t q_len, int32_t kv_len,
+                            int32_t hq, int32_t hkv, int32_t d, float scale, int32_t num_splits,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f)
+    return fail(BCA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  bca::DecodeArgs a;
+  const bca_status_t st = decode_args(q, k8, v8, o, lse, q_len, kv_len, hq, hkv, d, scale,
+                                      BCA_BF16, num_splits, workspace, ws_bytes, &a);
+  if (st != BCA_OK) return st;
+  a.k8 = static_cast<const uint8_t*>(k8);
+  a.v8 = static_cast<const uint8_t*>(v8);
+  a.k = nullptr;
+  a.v = nullptr;
+  a.scale_log2 *= k_scale;
+  a.o_mul = v_scale;
+  return hip_status(bca::launch_decode_fp8(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
 bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,

@@ -41,8 +41,11 @@ struct FwdF32Args {
 
 struct DecodeArgs {
   const uint16_t* q;  // [q_len, hq, d]
-  const uint16_t* k;  // [kv_len, hkv, d]
+  const uint16_t* k;  // [kv_len, hkv, d] bf16 (decode_bf16_kernel)
   const uint16_t* v;
+  const uint8_t* k8;  // [kv_len, hkv, d] fp8 E4M3 (decode_fp8_kernel)
+  const uint8_t* v8;
+  float o_mul;        // multiplies O (the V scale of an fp8 cache; 1 for bf16)
   uint16_t* o;        // [q_len, hq, d]
   float* lse;         // [hq, q_len]
   // Split partials (nsplit > 1), per (split, head, 32-token tile):
@@ -88,6 +91,7 @@ inline int heads_per_wg(int hq, int hkv) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int max_seqlen, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdF32Args& a, int max_seqlen, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream);
 
 }  // namespace bca

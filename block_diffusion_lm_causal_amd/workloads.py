@@ -167,6 +167,30 @@ def decode_step(prefix_len: int, block_size: int = 32, hq: int = 32, hkv: int = 
                     prefix_lens=np.array([prefix_len]), seed=seed)
 
 
+def decode_step_fp8(prefix_len: int, block_size: int = 32, hq: int = 32, hkv: int = 8,
+                    d: int = 128, seed: int = 7):
+    """Decode step against an FP8 E4M3 cache: returns (workload, k8, v8, k_scale, v_scale).
+
+    K and V are drawn as for decode_step, then stored as E4M3 bytes of
+    K / k_scale and V / v_scale with per-tensor scales max|x| / 448 (the
+    largest E4M3 value), rounded to nearest even by torch's CPU cast; the
+    workload's k and v hold the decoded values k_scale * e4m3 (float32).
+    """
+    w = decode_step(prefix_len, block_size, hq, hkv, d, seed)
+    rng = np.random.default_rng(seed + 1000)
+    kv_len = prefix_len + block_size
+    k = torch.from_numpy(rng.standard_normal((kv_len, hkv, d), dtype=np.float32))
+    v = torch.from_numpy(rng.standard_normal((kv_len, hkv, d), dtype=np.float32))
+    k_scale = float(k.abs().max()) / 448.0
+    v_scale = float(v.abs().max()) / 448.0
+    k8 = (k / k_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    v8 = (v / v_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    w.k = k8.view(torch.float8_e4m3fn).float() * k_scale
+    w.v = v8.view(torch.float8_e4m3fn).float() * v_scale
+    w.name = f"decode_fp8_P{prefix_len}_B{block_size}_gqa{hq}x{hkv}_d{d}"
+    return w, k8, v8, k_scale, v_scale
+
+
 def staircase_fwd_8traj() -> Workload:
     """8 trajectories, prefix 32*U{16..128}, S = U{4..24} copies of a 32-token block, seed 3."""
     rng = np.random.default_rng(3)

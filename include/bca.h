@@ -205,6 +205,21 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
                         size_t ws_bytes, void* stream);
 
 /*
+ * Decode step against an FP8 KV cache (the pages serve with an FP8 KV cache:
+ * paper cards page, Table 11 configurations).  As bca_decode, except
+ *   k8, v8            : [kv_len, hkv, d] bytes, OCP FP8 E4M3 (bias 7, no
+ *                       infinities, S.1111.111 is NaN), 16-byte aligned
+ *   k_scale, v_scale  : the cache holds K / k_scale and V / v_scale: the keys
+ *                       and values attended are k_scale * e4m3(k8) and
+ *                       v_scale * e4m3(v8) (finite, > 0)
+ * q, o stay bf16; the workspace is bca_decode_workspace's (same partials).
+ */
+bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float k_scale,
+                            float v_scale, void* o, float* lse, int32_t q_len, int32_t kv_len,
+                            int32_t hq, int32_t hkv, int32_t d, float scale, int32_t num_splits,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Captured denoising loop (thread page, Result 4: each block's denoising loop
  * runs on the GPU as one captured graph, so per-step launch and scheduling
  * costs vanish at batch 1).  bca_decode_graph_create checks its arguments as

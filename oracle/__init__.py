@@ -14,7 +14,8 @@ and torch autograd for the gradients, and the invariants of softmax attention.
 from .attention import (allowed_matrix, allowed_matrix_groups, attention_bwd,
                         attention_dq_rows, attention_fwd, decode, segment_allowed,
                         segment_prefix_len)
+from .fp8 import e4m3_to_float
 from .packing import lpt, optimal_makespan, trajectory_cost
 
 __all__ = ["allowed_matrix", "allowed_matrix_groups", "segment_allowed", "attention_bwd", "attention_dq_rows", "attention_fwd", "decode",
-           "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost"]
+           "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost", "e4m3_to_float"]

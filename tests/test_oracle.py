@@ -485,3 +485,24 @@ def test_group_pair_count_matches_mask():
     want = sum(int(oracle.segment_allowed(int(L), g, 8).sum())
                for L, g in zip(np.diff(w.cu_seqlens), w.groups))
     assert W.useful_pairs_groups(np.diff(w.cu_seqlens), w.groups, 8) == want
+
+
+# --------------------------------------------------------------------------- FP8 E4M3
+
+def test_e4m3_special_values_by_hand():
+    f = oracle.e4m3_to_float
+    assert f(0x00) == 0.0 and np.signbit(f(0x80))
+    assert f(0x01) == 2.0 ** -9 and f(0x07) == 7 * 2.0 ** -9      # subnormals
+    assert f(0x08) == 2.0 ** -6                                    # smallest normal
+    assert f(0x38) == 1.0 and f(0xB8) == -1.0
+    assert f(0x7E) == 448.0 and f(0xFE) == -448.0                  # largest finite
+    assert np.isnan(f(0x7F)) and np.isnan(f(0xFF))
+
+
+def test_e4m3_matches_torch_float8_for_all_bytes():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_to_float(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
