@@ -12,7 +12,8 @@ under ``"paths"``:
   * decode step, 32 queries against a prefix of 1024 or 8192 keys plus the
     block's own 32 (GQA 32/8, d 128): HBM GB/s of the algorithmic bytes
     (K and V read once per KV head, Q read, O and LSE written), median over
-    32 calls with L2 and the Infinity Cache flushed before each call, plus the
+    32 calls with L2 and the Infinity Cache flushed (by reading 512 MB)
+    before each call, plus the
     warm back-to-back figure and the per-step time of a captured 32-step
     graph (caches warm), labelled; the same against an FP8 E4M3 cache;
   * staircase forward, 8 packed trajectories (block 32);
@@ -81,7 +82,7 @@ def stored_traffic(kernel_tag: str):
 
 def timed_calls(fn, steps: int, warmup: int, flush=None):
     """Run fn() warmup + steps times; returns (per-call event ms list, wall ms of the
-    timed region).  With flush, the cache-flush write runs before every timed call,
+    timed region).  With flush, the cache flush runs before every timed call,
     outside its events, and the wall figure is not meaningful."""
     import torch
     # W warm-up calls, continued until about a second of work has run so the GPU
@@ -128,6 +129,16 @@ def bench_prefill(steps: int, warmup: int):
     return w, flops, per_call, wall
 
 
+def make_flush(dev):
+    """Evict L2 and the Infinity Cache before a timed call by READING 512 MB
+    (a decode loop streams the model's weights between steps).  A write-based
+    flush would leave dirty lines whose write-back competes with the call."""
+    import torch
+    buf = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    return lambda: sink.copy_(buf.sum())
+
+
 def bench_decode(prefix: int, calls: int = 32):
     import torch
     from block_diffusion_lm_causal_amd import bca, workloads
@@ -141,12 +152,12 @@ def bench_decode(prefix: int, calls: int = 32):
     kv_len = prefix + w.block_size
     algo_bytes = (2 * kv_len * w.hkv * w.d * 2 + 2 * w.block_size * w.hq * w.d * 2
                   + w.hq * w.block_size * 4)
-    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = make_flush(dev)
 
     def step():
         bca.decode(q, k, v, w.scale, workspace=ws, out=o, lse=lse)
 
-    cold, _ = timed_calls(step, calls, 3, flush=lambda: flush_buf.fill_(1.0))
+    cold, _ = timed_calls(step, calls, 3, flush=flush)
     warm, _ = timed_calls(step, calls, 3)
     cold_us = statistics.median(cold) * 1e3
     warm_us = statistics.median(warm) * 1e3
@@ -182,12 +193,12 @@ def bench_decode_fp8(prefix: int, calls: int = 32):
     lse = torch.empty((w.hq, w.block_size), dtype=torch.float32, device=dev)
     algo_bytes = (2 * kv_len * w.hkv * w.d + 2 * w.block_size * w.hq * w.d * 2
                   + w.hq * w.block_size * 4)
-    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = make_flush(dev)
 
     def step():
         bca.decode_fp8(q, k8, v8, ks, vs, w.scale, workspace=ws, out=o, lse=lse)
 
-    cold, _ = timed_calls(step, calls, 3, flush=lambda: flush_buf.fill_(1.0))
+    cold, _ = timed_calls(step, calls, 3, flush=flush)
     warm, _ = timed_calls(step, calls, 3)
     cold_us = statistics.median(cold) * 1e3
     warm_us = statistics.median(warm) * 1e3
