@@ -812,72 +812,89 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   dec_finish<D>(a, dw, reinterpret_cast<float*>(&lds.k8[0][0]), ws);
 }
 
-// Merge the split partials: one wave per (head, 32-token tile, 1 KB slice of
-// the partial), so that the merge runs on many compute units at once.  Lane l
-// serves token l % 32; lse = log sum_c exp(lse_c), O = sum_c exp(lse_c - lse) O_c.
-constexpr int kCombineMaxSplits = 256;
+// Merge the split partials: one 4-wave workgroup per (head, 32-token tile,
+// 1 KB slice of the partial), so that the merge runs on many compute units
+// with several loads in flight per lane.  Wave w takes the splits c = w mod 4;
+// lane l serves token l % 32.  Each wave forms lse_w = log sum exp(lse_c) and
+// O_w = sum_c exp(lse_c - lse_w) O_c over its splits (the loads of up to
+// kChunk splits issued together), then wave 0 merges the four (lse_w, O_w)
+// the same way through LDS.
+constexpr int kCombineWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  __shared__ float wts[kCombineMaxSplits][32];  // log2-domain lse, then exp weights
-  constexpr int kSlices = D / 8;                // 1 KB slices of a 32 x D fp32 partial
+__global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int kSlices = D / 8;  // 1 KB slices of a 32 x D fp32 partial
+  constexpr int kChunk = 8;
+  __shared__ f32x4 red_o[kCombineWaves][64];
+  __shared__ float red_m[kCombineWaves][64], red_s[kCombineWaves][64];
   const int ntok32 = (a.q_len + 31) / 32;
   const int slice = blockIdx.x % kSlices;
   const int rest = blockIdx.x / kSlices;
   const int tile = rest % ntok32;
   const int head = rest / ntok32;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int row = lane & 31;
   const size_t tile_stride = (size_t)a.hq * ntok32;  // partial tiles per split
   const size_t my_tile = (size_t)head * ntok32 + tile;
   const float* lse_src = a.part_lse + my_tile * 32 + row;
-  float m = kNegBig;
-  int c = 0;
-  for (; c + 8 <= a.nsplit; c += 8) {
-    float x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = lse_src[(size_t)(c + u) * tile_stride * 32] * kLog2e;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      m = fmaxf(m, x[u]);
-      if (lane < 32) wts[c + u][row] = x[u];
-    }
-  }
-  for (; c < a.nsplit; ++c) {
-    const float x = lse_src[(size_t)c * tile_stride * 32] * kLog2e;
-    m = fmaxf(m, x);
-    if (lane < 32) wts[c][row] = x;
-  }
-  __syncthreads();
-  float sum = 0.f;
-  for (int cc = 0; cc < a.nsplit; ++cc) {
-    const float wv = fast_exp2(wts[cc][row] - m);
-    sum += wv;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < 32) wts[cc][row] = wv;
-  }
-  __syncthreads();
-  const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + my_tile * (size_t)(32 * D)) +
-                     slice * 64 + lane;
-  const size_t split_stride = tile_stride * (size_t)(32 * D / 4);  // float4s
+  const f32x4* o_src = reinterpret_cast<const f32x4*>(a.part_o + my_tile * (size_t)(32 * D)) +
+                       slice * 64 + lane;
+  const size_t lse_step = tile_stride * 32;             // floats between splits
+  const size_t o_step = tile_stride * (size_t)(8 * D);  // float4s between splits
+  float m = kNegBig, sum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  c = 0;
-  for (; c + 8 <= a.nsplit; c += 8) {
-    f32x4 x[8];
+  for (int c0 = wave; c0 < a.nsplit; c0 += kChunk * kCombineWaves) {
+    float x[kChunk];
+    f32x4 y[kChunk];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = src[(size_t)(c + u) * split_stride];
+    for (int u = 0; u < kChunk; ++u) {
+      const int c = c0 + u * kCombineWaves;
+      x[u] = kNegBig;
+      y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < a.nsplit) {
+        x[u] = lse_src[(size_t)c * lse_step] * kLog2e;
+        y[u] = o_src[(size_t)c * o_step];
+      }
+    }
+    float mc = m;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc += wts[c + u][row] * x[u];
+    for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, x[u]);
+    const float sc = fast_exp2(m - mc);
+    acc *= sc;
+    sum *= sc;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float wv = fast_exp2(x[u] - mc);  // 0 for missing splits
+      acc += wv * y[u];
+      sum += wv;
+    }
+    m = mc;
   }
-  for (; c < a.nsplit; ++c) acc += wts[c][row] * src[(size_t)c * split_stride];
-  acc *= 1.f / sum;
+  red_o[wave][lane] = acc;
+  red_m[wave][lane] = m;
+  red_s[wave][lane] = sum;
+  __syncthreads();
+  if (wave != 0) return;
+  float mt = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) mt = fmaxf(mt, red_m[w][lane]);
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  float st = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineWaves; ++w) {
+    const float wv = fast_exp2(red_m[w][lane] - mt);
+    o += wv * red_o[w][lane];
+    st += wv * red_s[w][lane];
+  }
+  o *= 1.f / st;
   // slice = dt * 4 + g: dims 32 dt + 8 g + 4 (lane / 32) + 0..3 of token row
   const int qi = tile * 32 + row;
   if (qi < a.q_len) {
     const int d = (slice >> 2) * 32 + (slice & 3) * 8 + 4 * (lane >> 5);
     *reinterpret_cast<u32x2*>(a.o + ((size_t)qi * a.hq + head) * D + d) =
-        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    if (slice == 0 && lane < 32) a.lse[(size_t)head * a.q_len + qi] = (m + fast_log2(sum)) * kLn2;
+        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (slice == 0 && lane < 32) a.lse[(size_t)head * a.q_len + qi] = (mt + fast_log2(st)) * kLn2;
   }
 }
 
@@ -920,9 +937,11 @@ hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
   if (err != hipSuccess || a.nsplit == 1) return err;
   const unsigned ncomb = (unsigned)((a.q_len + 31) / 32) * a.hq * (a.d / 8);
   if (a.d == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(ncomb), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(ncomb), dim3(64 * kCombineWaves), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(ncomb), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(ncomb), dim3(64 * kCombineWaves), 0,
+                       stream, a);
   }
   return hipGetLastError();
 }
