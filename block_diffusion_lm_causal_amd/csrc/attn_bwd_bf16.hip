@@ -27,6 +27,8 @@
 //      waves, one phase apart, over 32-key tiles: MFMA phase S^T(t) = K Q^T,
 //      dP^T(t) = V dO^T and dQ^T += K^T dS^T(t-1); VALU phase P and dS of
 //      tile t.  K^T comes from the row-major K tile through the transposed read.
+#include <type_traits>
+
 #include "bca_device.hpp"
 #include "bca_kernels.hpp"
 
@@ -99,17 +101,32 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
 // ---------------------------------------------------------------------------
 // 2. dK / dV
 
-template <int D>
-struct KvLds {
-  uint16_t q[3][kQt * D];    // Q tile, row-major swizzled
-  uint16_t g[3][kQt * D];    // dO tile
+// Per-step side values of the dK/dV kernel (its Q/dO tiles are separate
+// arrays, see the kernel).
+struct KvSide {
   float lse2[3][kQt];        // LSE * log2(e) of the tile's rows
   float delta[3][kQt];
 };
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max) {
-  __shared__ KvLds<D> lds;
+  // Q and dO tiles (row-major, swizzled), three steps of each, as separate
+  // arrays: every access names its buffer at compile time (the step loop is
+  // unrolled by three), so a read of one buffer never waits for direct loads
+  // still in flight into another.
+  __shared__ __attribute__((aligned(16))) uint16_t q0s[kQt * D], q1s[kQt * D], q2s[kQt * D];
+  __shared__ __attribute__((aligned(16))) uint16_t g0s[kQt * D], g1s[kQt * D], g2s[kQt * D];
+  __shared__ KvSide lds;
+  auto qbuf = [&](auto bc) -> uint16_t* {
+    if constexpr (decltype(bc)::value == 0) return q0s;
+    else if constexpr (decltype(bc)::value == 1) return q1s;
+    else return q2s;
+  };
+  auto gbuf = [&](auto bc) -> uint16_t* {
+    if constexpr (decltype(bc)::value == 0) return g0s;
+    else if constexpr (decltype(bc)::value == 1) return g1s;
+    else return g2s;
+  };
   const int group = a.hq / a.hkv;
   // Order: KV head fastest, then the key tiles of one segment (earliest keys,
   // i.e. most query rows, first), then the next segment.  Every workgroup
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       }
     }
   };
-  auto issue_step = [&](const Cursor& c, int buf) {
+  auto issue_step = [&](const Cursor& c, auto bc) {
     const int qt0 = c.qt0;
     const int head = g * group + c.h;
     const int rows = min(c.end - qt0, kQt);
@@ -210,8 +227,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + off, nbytes);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
-      if (dma_is_q[j]) buffer_load_lds16(rq, &lds.q[buf][dma_row0[j] * D], dma_voff[j]);
-      else buffer_load_lds16(rg, &lds.g[buf][dma_row0[j] * D], dma_voff[j]);
+      if (dma_is_q[j]) buffer_load_lds16(rq, qbuf(bc) + dma_row0[j] * D, dma_voff[j]);
+      else buffer_load_lds16(rg, gbuf(bc) + dma_row0[j] * D, dma_voff[j]);
     }
   };
   // Wait until only the newest step's loads may be outstanding (wave 0 also
@@ -225,15 +242,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const int qt0 = c.qt0;
     const int head = g * group + c.h;
     const int i = qt0 + (lane & 31);
+    // raw values: scaling here would wait for the load at once
     float v = 0.f;
     if (i < c.end) {
-      v = half == 0 ? a.lse[(size_t)head * a.total + base + i] * kLog2e
+      v = half == 0 ? a.lse[(size_t)head * a.total + base + i]
                     : a.delta[(size_t)head * a.total + base + i];
     }
     return v;
   };
   auto store_side = [&](float v, int buf) {
-    if (half == 0) lds.lse2[buf][lane] = v;
+    if (half == 0) lds.lse2[buf][lane] = v * kLog2e;
     else lds.delta[buf][lane & 31] = v;
   };
 
@@ -302,11 +320,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   float side_next = 0.f, side_new = 0.f;
   if (nsteps > 0) {
     if (wave == 0) store_side(load_side(nxt), 0);
-    issue_step(nxt, 0);
+    issue_step(nxt, std::integral_constant<int, 0>{});
     advance(nxt);
     if (nsteps > 1) {
       if (wave == 0) side_next = load_side(nxt);
-      issue_step(nxt, 1);
+      issue_step(nxt, std::integral_constant<int, 1>{});
       advance(nxt);
     }
   }
@@ -314,11 +332,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   else wait_vmem();
   __syncthreads();
 
-  for (int st = 0, buf = 0; st < nsteps; ++st, buf = buf == 2 ? 0 : buf + 1) {
+  auto step = [&](int st, auto bc) {
+    constexpr int buf = decltype(bc)::value;  // st % 3
+    // Side values first: an LDS read waits for every direct load in flight
+    // into an array the compiler cannot tell apart, so it goes before this
+    // step's loads are issued.  Register r4 group: rows 8 r4 + 4 half + 0..3.
+    f32x4 l2v[4], dlv[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      l2v[r4] = *reinterpret_cast<const f32x4*>(&lds.lse2[buf][8 * r4 + 4 * half]);
+      dlv[r4] = *reinterpret_cast<const f32x4*>(&lds.delta[buf][8 * r4 + 4 * half]);
+    }
     if (st + 2 < nsteps) {
-      const int buf2 = buf == 0 ? 2 : buf - 1;  // (st + 2) % 3
       if (wave == 0) side_new = load_side(nxt);
-      issue_step(nxt, buf2);
+      issue_step(nxt, std::integral_constant<int, (buf + 2) % 3>{});
       advance(nxt);
     }
     const int qt0 = cur.qt0, qe = cur.end;
@@ -327,8 +354,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     if (active) {
       const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
                                             (qt0 >= f2lo && qt0 + kQt <= f2hi));
-      const char* qtile = reinterpret_cast<const char*>(lds.q[buf]);
-      const char* gtile = reinterpret_cast<const char*>(lds.g[buf]);
+      const char* qtile = reinterpret_cast<const char*>(qbuf(bc));
+      const char* gtile = reinterpret_cast<const char*>(gbuf(bc));
       // S = Q K^T (and dP = dO V^T in K waves): queries on M, keys on N.
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -348,9 +375,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int q0r = 8 * r4 + 4 * half;
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&lds.lse2[buf][q0r]);
-        f32x4 dl = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kwave) dl = *reinterpret_cast<const f32x4*>(&lds.delta[buf][q0r]);
+        const f32x4 l2 = l2v[r4];
+        const f32x4 dl = dlv[r4];
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -381,8 +407,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       }
     }
     advance(cur);
-    // Step st+1's tile must have landed; step st+2's may still be in flight.
-    const int buf1 = buf == 2 ? 0 : buf + 1;
+    // Step st+1's tile must have landed; step st+2's stays in flight across
+    // the barrier.
+    constexpr int buf1 = (buf + 1) % 3;
     if (st + 2 < nsteps) {
       if (wave == 0) {
         store_side(side_next, buf1);
@@ -393,7 +420,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       if (wave == 0 && st + 1 < nsteps) store_side(side_next, buf1);
       wait_vmem();
     }
-    __syncthreads();
+    barrier_lds();
+  };
+  for (int st = 0; st < nsteps; st += 3) {
+    step(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
+    if (st + 2 < nsteps) step(st + 2, std::integral_constant<int, 2>{});
   }
 
   // Epilogue: lane holds dims 32 dt + lane%32 of keys 8(r/4) + 4 half + r%4.

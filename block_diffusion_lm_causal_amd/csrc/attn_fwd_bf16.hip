@@ -122,23 +122,6 @@ __device__ __forceinline__ void write_rows(const WaveState<D>& ws, bool valid, v
 
 constexpr int kPPThreads = 512;
 
-// Workgroup barrier that leaves direct-to-LDS loads in flight.  __syncthreads()
-// would wait for them: its release fence waits for every earlier memory
-// operation.  LDS reads issued before this barrier have returned (lgkmcnt),
-// so a buffer may be overwritten after it; the memory clobber keeps the
-// compiler from moving memory accesses across it.  Data of a direct load is
-// visible to other waves only once its issuer has waited for it (vmcnt) and
-// then passed a barrier.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// The same, after this wave's direct-to-LDS loads have landed.  Written as one
-// asm block so that the wait stays at the end of the phase.
-__device__ __forceinline__ void wait_vmem_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <int D>
 struct LdsPP {
   uint16_t k[2][kBN * D];

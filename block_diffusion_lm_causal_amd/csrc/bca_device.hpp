@@ -66,6 +66,23 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// Workgroup barrier that leaves direct-to-LDS loads in flight.  __syncthreads()
+// would wait for them: its release fence waits for every earlier memory
+// operation.  LDS reads issued before this barrier have returned (lgkmcnt),
+// so a buffer may be overwritten after it; the memory clobber keeps the
+// compiler from moving memory accesses across it.  Data of a direct load is
+// visible to other waves only once its issuer has waited for it (vmcnt) and
+// then passed a barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The same, after this wave's direct-to-LDS loads have landed.  Written as one
+// asm block so that the wait stays at the end of the phase.
+__device__ __forceinline__ void wait_vmem_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // 16-byte chunk swizzle of a row-major tile with D/8 chunks per row: chunk c
 // of row r is stored at chunk c ^ swz(r).  Chosen so that 16 consecutive rows
 // read at one logical chunk, and 4 consecutive rows read at 4 consecutive
