@@ -497,26 +497,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
   auto tile_k0 = [&](int t) { return t < n1 ? t * kBN : tk.r2s + (t - n1) * kBN; };
   auto tile_end = [&](int t) { return t < n1 ? tk.r1e : tk.r2e; };
 
-  // DMA: a kBN x D tile is kBN*D*2/1024 instructions per tensor; wave w issues
-  // instruction w of each tensor (waves past the count issue none).
+  // DMA, by the four waves of group A only: a kBN x D tile is kInstPerTensor
+  // 1 KB instructions per tensor; wave w issues instructions w + 4 j.
   constexpr int kChunks = D / 8;
   constexpr int kRowsPerInst = 64 / kChunks;
   constexpr int kInstPerTensor = kBN / kRowsPerInst;  // 8 (D=128) or 4 (D=64)
-  const bool dma_wave = wave < kInstPerTensor;
-  const int drow0 = wave * kRowsPerInst;
-  const uint32_t dvoff = [&] {
-    const int R = drow0 + lane / kChunks;
-    return (uint32_t)(R * kv_elems * 2 + (((lane % kChunks) ^ swz<D>(R)) * 16));
-  }();
+  constexpr int kInstPerWave = kInstPerTensor / 4;
+  uint32_t dvoff[kInstPerWave];
+  int drow0[kInstPerWave];
+#pragma unroll
+  for (int j = 0; j < kInstPerWave; ++j) {
+    drow0[j] = ((wave & 3) + 4 * j) * kRowsPerInst;
+    const int R = drow0[j] + lane / kChunks;
+    dvoff[j] = (uint32_t)(R * kv_elems * 2 + (((lane % kChunks) ^ swz<D>(R)) * 16));
+  }
   auto issue = [&](const uint16_t* src, int t, uint16_t* dst) {
-    if (!dma_wave) return;
     const int k0 = tile_k0(t);
     const int rows = min(tile_end(t) - k0, kBN);
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(src + (size_t)k0 * kv_elems, (uint32_t)((rows - 1) * kv_elems * 2 + D * 2));
-    buffer_load_lds16(r, dst + drow0 * D, dvoff);
+#pragma unroll
+    for (int j = 0; j < kInstPerWave; ++j) buffer_load_lds16(r, dst + drow0[j] * D, dvoff[j]);
   };
-  if (ntile > 0) {
+  if (ntile > 0 && grp == 0) {
     issue(kb, 0, lds.k[0]);
     issue(vb, 0, lds.v[0]);
   }
@@ -563,80 +566,95 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
     __syncthreads();
     f32x16 s[kBN / 32], dp[kBN / 32];
     uint32_t pk[kBN / 16][4];  // dS^T of the tile between its VALU and dQ phases
-    const int nphase = 2 * ntile + 2;
-    for (int phi = 0; phi < nphase; ++phi) {
-      if ((phi & 1) == 0) {
-        const int t = phi >> 1;
-        if (t + 1 < ntile) {
-          issue(kb, t + 1, lds.k[(t + 1) % 3]);
-          issue(vb, t + 1, lds.v[(t + 1) & 1]);
+    // MFMA phase: dQ^T += K^T dS^T of tile t-1 (t >= 1), then S^T and dP^T of
+    // tile t (t < ntile).
+    auto mfma_phase = [&](int t, bool do_dq, bool do_s) {
+      if (do_dq) {
+        const char* kt = reinterpret_cast<const char*>(lds.k[(t - 1) % 3]);
+#pragma unroll
+        for (int c = 0; c < kBN / 16; ++c) {
+          const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const bf16x8 ka = tr_pair(kt + toff[dt][0] + c * 16 * D * 2,
+                                      kt + toff[dt][1] + c * 16 * D * 2);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db, acc[dt], 0, 0, 0);
+          }
         }
       }
-      const int my = phi - grp;
-      if (my >= 0 && (my & 1) == 0) {
-        // MFMA phase for tile tm: dQ^T += K^T dS^T of tile tm-1, then S^T and dP^T of tm.
-        const int tm = my >> 1;
-        if (tm >= 1) {
-          const char* kt = reinterpret_cast<const char*>(lds.k[(tm - 1) % 3]);
-#pragma unroll
-          for (int c = 0; c < kBN / 16; ++c) {
-            const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-              const bf16x8 ka = tr_pair(kt + toff[dt][0] + c * 16 * D * 2,
-                                        kt + toff[dt][1] + c * 16 * D * 2);
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db, acc[dt], 0, 0, 0);
-            }
-          }
-        }
-        if (tm < ntile) {
-          const char* kt = reinterpret_cast<const char*>(lds.k[tm % 3]);
-          const char* vt = reinterpret_cast<const char*>(lds.v[tm & 1]);
-#pragma unroll
-          for (int h = 0; h < kBN / 32; ++h) {
-            s[h] = f32x16{};
-            dp[h] = f32x16{};
-          }
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-            for (int h = 0; h < kBN / 32; ++h) {
-              const uint32_t off = koff[kk] + h * 32 * D * 2;
-              const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
-              const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
-              s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[h], 0, 0, 0);
-              dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp[h], 0, 0, 0);
-            }
-          }
-        }
-      } else if (my >= 0 && (my >> 1) < ntile) {
-        // VALU phase for tile tv: P^T and dS^T.
-        const int tv = my >> 1;
-        const int k0 = tile_k0(tv), kend = tile_end(tv);
-        const bool full = wave_active && (k0 + kBN <= kend) &&
-                          ((k0 + kBN <= e1_all) ||
-                           (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+      if (do_s) {
+        const char* kt = reinterpret_cast<const char*>(lds.k[t % 3]);
+        const char* vt = reinterpret_cast<const char*>(lds.v[t & 1]);
 #pragma unroll
         for (int h = 0; h < kBN / 32; ++h) {
+          s[h] = f32x16{};
+          dp[h] = f32x16{};
+        }
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float dsv[2];
+        for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              float p = fast_exp2(fmaf(s[h][r + e], a.scale_log2, -lse2));
-              if (!full) {
-                const int j = k0 + h * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-                const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
-                p = ok ? p : 0.f;
-              }
-              dsv[e] = p * (dp[h][r + e] - dl);
-            }
-            pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
+          for (int h = 0; h < kBN / 32; ++h) {
+            const uint32_t off = koff[kk] + h * 32 * D * 2;
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
+            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[h], 0, 0, 0);
+            dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp[h], 0, 0, 0);
           }
         }
       }
-      if (phi & 1) wait_vmem();
-      __syncthreads();
+    };
+    // VALU phase of tile t: P^T and dS^T.
+    auto valu_phase = [&](int t) {
+      const int k0 = tile_k0(t), kend = tile_end(t);
+      const bool full = wave_active && (k0 + kBN <= kend) &&
+                        ((k0 + kBN <= e1_all) ||
+                         (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+#pragma unroll
+      for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float p = fast_exp2(fmaf(s[h][r + e], a.scale_log2, -lse2));
+            if (!full) {
+              const int j = k0 + h * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
+              const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+              p = ok ? p : 0.f;
+            }
+            dsv[e] = p * (dp[h][r + e] - dl);
+          }
+          pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
+        }
+      }
+    };
+    // Group A's loads in phase 2t, after its own LDS reads: K and V of tile t+1.
+    // The barrier closing phase 2t leaves them in flight; A waits for them at
+    // the end of phase 2t+1.
+    auto issue_next = [&](int t) {
+      if (t + 1 < ntile) {
+        issue(kb, t + 1, lds.k[(t + 1) % 3]);
+        issue(vb, t + 1, lds.v[(t + 1) & 1]);
+      }
+    };
+    // Two groups one phase apart, each in its own straight-line loop (as the
+    // forward): A runs MFMA(t) then VALU(t), B runs VALU(t-1) then MFMA(t);
+    // every iteration passes two barriers in both groups.
+    if (grp == 0) {
+      for (int t = 0; t <= ntile; ++t) {
+        mfma_phase(t, t >= 1, t < ntile);
+        issue_next(t);
+        barrier_lds();
+        if (t < ntile) valu_phase(t);
+        wait_vmem_barrier();
+      }
+    } else {
+      for (int t = 0; t <= ntile; ++t) {
+        if (t >= 1) valu_phase(t - 1);
+        barrier_lds();
+        mfma_phase(t, t >= 1, t < ntile);
+        barrier_lds();
+      }
     }
   }
 
