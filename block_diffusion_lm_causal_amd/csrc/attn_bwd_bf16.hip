@@ -13,13 +13,14 @@
 // Three kernels, no atomics (results are bit-reproducible):
 //   1. delta = rowsum(dO * O) in float32.
 //   2. dK/dV: an 8-wave workgroup owns 128 keys of one KV head.  Waves 0-3
-//      ("V waves", 32 keys each) compute S = Q K^T -> P -> dV += P^T dO;
-//      waves 4-7 ("K waves", the same keys) compute S and dP = dO V^T ->
-//      dS -> dK += dS^T Q.  Each SIMD pairs one wave of each kind, so one's
-//      MFMA work overlaps the other's exponentials.  K and V fragments and the
-//      dK/dV accumulators stay in registers; each step streams a 32-row tile
-//      of Q and dO (one query head) through LDS, loaded straight from HBM two
-//      steps ahead.  S is computed with queries on the M axis, so the P and dS
+//      ("V waves", 32 keys each) compute S = Q K^T -> P and dV += P^T dO;
+//      waves 4-7 ("K waves", the same keys) compute dP = dO V^T, take P from
+//      their V wave through LDS, form dS and dK += dS^T Q.  S is computed
+//      once, and each SIMD pairs one wave of each kind, so one's MFMA work
+//      overlaps the other's exponentials.  K and V fragments and the dK/dV
+//      accumulators stay in registers; each step streams a 32-row tile of Q
+//      and dO (one query head) through LDS, loaded straight from HBM two steps
+//      ahead.  S is computed with queries on the M axis, so the P and dS
 //      accumulators are, unchanged, the A operands of the dV and dK products;
 //      their B operands (dO and Q with queries on K) come from the row-major
 //      tiles through the transposed LDS read.
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   __shared__ __attribute__((aligned(16))) uint16_t q0s[kQt * D], q1s[kQt * D], q2s[kQt * D];
   __shared__ __attribute__((aligned(16))) uint16_t g0s[kQt * D], g1s[kQt * D], g2s[kQt * D];
   __shared__ KvSide lds;
+  __shared__ uint32_t p_xchg[4][8 * 64];  // P (bf16 pairs) from V wave to K wave, per key quarter
   auto qbuf = [&](auto bc) -> uint16_t* {
     if constexpr (decltype(bc)::value == 0) return q0s;
     else if constexpr (decltype(bc)::value == 1) return q1s;
@@ -351,49 +353,70 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     const int qt0 = cur.qt0, qe = cur.end;
     const bool active = wave_has_keys && ((qt0 < w1hi && qt0 + kQt > w1lo) ||
                                           (qt0 < w2hi && qt0 + kQt > w2lo));
+    // V waves compute S = Q K^T and P (masked, bf16) and hand P to the K wave
+    // of the same 32 keys through LDS; K waves compute dP = dO V^T meanwhile.
+    // After the barrier the V wave accumulates dV += P^T dO and the K wave
+    // forms dS = P (dP - delta) and accumulates dK += dS^T Q (keys on M, dims
+    // on N, queries contracted, the B operand through the transposed read).
+    // Register r of a lane holds query row 8(r/4) + 4 half + r%4.
+    const char* qtile = reinterpret_cast<const char*>(qbuf(bc));
+    const char* gtile = reinterpret_cast<const char*>(gbuf(bc));
+    uint32_t pk[2][4];
+    f32x16 dp = f32x16{};
+    uint32_t* pex = &p_xchg[wave & 3][0];
     if (active) {
-      const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
-                                            (qt0 >= f2lo && qt0 + kQt <= f2hi));
-      const char* qtile = reinterpret_cast<const char*>(qbuf(bc));
-      const char* gtile = reinterpret_cast<const char*>(gbuf(bc));
-      // S = Q K^T (and dP = dO V^T in K waves): queries on M, keys on N.
-      f32x16 s = f32x16{}, dp = f32x16{};
+      if (!kwave) {
+        const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
+                                              (qt0 >= f2lo && qt0 + kQt <= f2hi));
+        f32x16 sc = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qtile + roff[kk]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kf[kk], s, 0, 0, 0);
-      }
-      if (kwave) {
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qtile + roff[kk]);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kf[kk], sc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int q0r = 8 * r4 + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = fast_exp2(fmaf(sc[4 * r4 + e], a.scale_log2, -l2v[r4][e]));
+            if (!full) {
+              const int i = qt0 + q0r + e;
+              const bool ok = (i < qe) & row_sees(kr, i);
+              pv = ok ? pv : 0.f;
+            }
+            v[e] = pv;
+          }
+          pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
+          pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pex[j * 64 + lane] = pk[j >> 2][j & 3];
+      } else {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const bf16x8 ga8 = *reinterpret_cast<const bf16x8*>(gtile + roff[kk]);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga8, vf[kk], dp, 0, 0, 0);
         }
       }
-      // P (and dS); register r holds query row 8(r/4) + 4 half + r%4.
-      uint32_t pk[2][4];
+    }
+    barrier_lds();  // P of every key quarter is in LDS
+    if (active) {
+      if (kwave) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int q0r = 8 * r4 + 4 * half;
-        const f32x4 l2 = l2v[r4];
-        const f32x4 dl = dlv[r4];
-        float v[4];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const uint32_t w0 = pex[((r4 >> 1) * 4 + (r4 & 1) * 2 + 0) * 64 + lane];
+          const uint32_t w1 = pex[((r4 >> 1) * 4 + (r4 & 1) * 2 + 1) * 64 + lane];
+          const float p[4] = {bf16_to_f32(w0 & 0xffffu), bf16_to_f32(w0 >> 16),
+                              bf16_to_f32(w1 & 0xffffu), bf16_to_f32(w1 >> 16)};
+          float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float pv = fast_exp2(fmaf(s[r], a.scale_log2, -l2[e]));
-          if (!full) {
-            const int i = qt0 + q0r + e;
-            const bool ok = (i < qe) & row_sees(kr, i);
-            pv = ok ? pv : 0.f;
-          }
-          v[e] = kwave ? pv * (dp[r] - dl[e]) : pv;
+          for (int e = 0; e < 4; ++e) v[e] = p[e] * (dp[4 * r4 + e] - dlv[r4][e]);
+          pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
+          pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
         }
-        pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
-        pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
       }
-      // dV += P^T dO (V waves) or dK += dS^T Q (K waves): keys on M, dims on N,
-      // queries contracted; B operand through the transposed read.
       const char* btile = kwave ? qtile : gtile;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
