@@ -24,6 +24,7 @@ SOURCES = [
     "bca_api.cpp",
     "bca_pack.cpp",
     "attn_fwd_bf16.hip",
+    "attn_decode_bf16.hip",
     "attn_fwd_f32.hip",
     "attn_bwd_bf16.hip",
 ]
