@@ -41,7 +41,7 @@ constexpr int kQt = 32;    // query rows per dK/dV step
 constexpr int kKvKeys = 128;  // keys per dK/dV workgroup
 
 // ---------------------------------------------------------------------------
-// 1. delta[h][i] = sum_d dO[i,h,d] * O[i,h,d]
+// 1. delta[h][i] = sum_d dO[i,h,d] * O[i,h,d], and lse2[h][i] = LSE[h][i] log2(e)
 
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int d = a.d;
@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
     const long long i = row / a.hq;
     const int h = (int)(row % a.hq);
     a.delta[(size_t)h * a.total + i] = acc;
+    a.lse2[(size_t)h * a.total + i] = a.lse[(size_t)h * a.total + i] * kLog2e;
   }
 }
 
@@ -102,33 +103,24 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* p0, const char* p1) {
 // ---------------------------------------------------------------------------
 // 2. dK / dV
 
-// Per-step side values of the dK/dV kernel (its Q/dO tiles are separate
-// arrays, see the kernel).
-struct KvSide {
-  float lse2[3][kQt];        // LSE * log2(e) of the tile's rows
-  float delta[3][kQt];
+// Per-tile side values of the dK/dV kernel: [buffer][0] the LSE of the
+// tile's rows times log2(e), [buffer][1] their delta (64 slots, rows past the
+// tile's 32 land in the upper half and are not read).
+struct __attribute__((aligned(16))) KvSide {
+  float v[4][2][64];
 };
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max) {
-  // Q and dO tiles (row-major, swizzled), three steps of each, as separate
-  // arrays: every access names its buffer at compile time (the step loop is
-  // unrolled by three), so a read of one buffer never waits for direct loads
-  // still in flight into another.
-  __shared__ __attribute__((aligned(16))) uint16_t q0s[kQt * D], q1s[kQt * D], q2s[kQt * D];
-  __shared__ __attribute__((aligned(16))) uint16_t g0s[kQt * D], g1s[kQt * D], g2s[kQt * D];
+  // Four tile buffers, each a Q tile then a dO tile (32 rows x D, row-major,
+  // swizzled), filled by direct loads that the compiler does not see (so it
+  // adds no waits for them); explicit waits and barriers order them.
+  constexpr int kTileBytes = 2 * kQt * D * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4][2 * kQt * D];
   __shared__ KvSide lds;
-  __shared__ uint32_t p_xchg[4][8 * 64];  // P (bf16 pairs) from V wave to K wave, per key quarter
-  auto qbuf = [&](auto bc) -> uint16_t* {
-    if constexpr (decltype(bc)::value == 0) return q0s;
-    else if constexpr (decltype(bc)::value == 1) return q1s;
-    else return q2s;
-  };
-  auto gbuf = [&](auto bc) -> uint16_t* {
-    if constexpr (decltype(bc)::value == 0) return g0s;
-    else if constexpr (decltype(bc)::value == 1) return g1s;
-    else return g2s;
-  };
+  // P of a tile (bf16 pairs, two 16-byte words per lane) from each V wave to
+  // the K wave of the same keys, double-buffered by step parity.
+  __shared__ __attribute__((aligned(16))) uint32_t p_xchg[2][4][2][64 * 4];
   const int group = a.hq / a.hkv;
   // Order: KV head fastest, then the key tiles of one segment (earliest keys,
   // i.e. most query rows, first), then the next segment.  Every workgroup
@@ -182,8 +174,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 
   // Loads: Q and dO tiles (32 rows x D) by DMA.  A tile is kInstPerTile
   // 1 KB instructions per tensor; instruction i of the 2 * kInstPerTile is
-  // issued by wave i % 8 (Q blocks first, then dO blocks).  LSE/delta rows are
-  // loaded by wave 0 with plain loads.
+  // issued by wave i % 8 (Q blocks first, then dO blocks).  Wave 0 also loads
+  // the tile's LSE * log2(e) and delta rows (two 256-byte loads).
   constexpr int kChunks = D / 8;
   constexpr int kRowsPerInst = 64 / kChunks;               // 4 (D=128) or 8 (D=64)
   constexpr int kInstPerTile = kQt / kRowsPerInst;         // 8 or 4
@@ -219,70 +211,72 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       }
     }
   };
-  auto issue_step = [&](const Cursor& c, auto bc) {
+  const uint32_t tiles_lds = lds_addr_of(&tiles[0][0]);
+  const uint32_t side_lds = lds_addr_of(&lds.v[0][0][0]);
+  auto issue_step = [&](const Cursor& c, int buf) {
     const int qt0 = c.qt0;
     const int head = g * group + c.h;
     const int rows = min(c.end - qt0, kQt);
     const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
     const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + off, nbytes);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.dout + off, nbytes);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
-      if (dma_is_q[j]) buffer_load_lds16(rq, qbuf(bc) + dma_row0[j] * D, dma_voff[j]);
-      else buffer_load_lds16(rg, gbuf(bc) + dma_row0[j] * D, dma_voff[j]);
+      const i32x4 r = rsrc_words((dma_is_q[j] ? a.q : a.dout) + off, nbytes);
+      const uint32_t dst = tiles_lds + (uint32_t)(buf * kTileBytes) +
+                           (dma_is_q[j] ? 0u : (uint32_t)(kQt * D * 2)) +
+                           (uint32_t)(dma_row0[j] * D * 2);
+      buffer_load_lds16_asm(r, dst, dma_voff[j]);
+    }
+    if (wave == 0) {
+      const size_t so = (size_t)head * a.total + base + qt0;
+      const uint32_t sbytes = (uint32_t)(rows * 4);
+      const uint32_t dst = side_lds + (uint32_t)(buf * 2 * 64 * 4);
+      buffer_load_lds4_asm(rsrc_words(a.lse2 + so, sbytes), dst, (uint32_t)lane * 4);
+      buffer_load_lds4_asm(rsrc_words(a.delta + so, sbytes), dst + 64 * 4, (uint32_t)lane * 4);
     }
   };
-  // Wait until only the newest step's loads may be outstanding (wave 0 also
-  // has its LSE/delta load in that step).
+  // Wait until only the newest step's loads may be outstanding.
   auto wait_all_but_newest = [&]() {
-    if (wave == 0) wait_vmem_le<kDmaPerWave + 1>();
+    if (wave == 0) wait_vmem_le<kDmaPerWave + 2>();
     else wait_vmem_le<kDmaPerWave>();
   };
-  auto load_side = [&](const Cursor& c) -> float {
-    // wave 0: lanes 0-31 the LSE of the tile's rows (scaled by log2 e), 32-63 delta
-    const int qt0 = c.qt0;
-    const int head = g * group + c.h;
-    const int i = qt0 + (lane & 31);
-    // raw values: scaling here would wait for the load at once
-    float v = 0.f;
-    if (i < c.end) {
-      v = half == 0 ? a.lse[(size_t)head * a.total + base + i]
-                    : a.delta[(size_t)head * a.total + base + i];
-    }
-    return v;
-  };
-  auto store_side = [&](float v, int buf) {
-    if (half == 0) lds.lse2[buf][lane] = v * kLog2e;
-    else lds.delta[buf][lane & 31] = v;
-  };
 
-  // K and V fragments of this wave's keys (B operands of S = Q K^T and dP = dO V^T).
-  bf16x8 kf[D / 16], vf[D / 16];
+  // K fragments of this wave's keys in V waves (B operand of S = Q K^T), V
+  // fragments in K waves (B operand of dP = dO V^T).
+  bf16x8 kvf[D / 16];
+  {
+    const uint16_t* src = kwave ? a.v : a.k;
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 rk = u32x4{0, 0, 0, 0}, rv = u32x4{0, 0, 0, 0};
-    if (key < L) {
-      const size_t off = ((size_t)(base + key) * a.hkv + g) * D + kk * 16 + half * 8;
-      rk = *reinterpret_cast<const u32x4*>(a.k + off);
-      if (kwave) rv = *reinterpret_cast<const u32x4*>(a.v + off);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 r = u32x4{0, 0, 0, 0};
+      if (key < L) {
+        const size_t off = ((size_t)(base + key) * a.hkv + g) * D + kk * 16 + half * 8;
+        r = *reinterpret_cast<const u32x4*>(src + off);
+      }
+      kvf[kk] = __builtin_bit_cast(bf16x8, r);
     }
-    kf[kk] = __builtin_bit_cast(bf16x8, rk);
-    vf[kk] = __builtin_bit_cast(bf16x8, rv);
   }
   f32x16 acc[D / 32];  // dV (V waves) or dK (K waves): keys on M, dims on N
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  uint32_t roff[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) roff[kk] = row_frag_off<D>(lane, kk);
+  // LDS offsets of this lane's fragments in a row-major swizzled tile, with
+  // the tensor each role reads folded in: the A operand of S / dP comes from
+  // the Q rows (V waves) or the dO rows (K waves), the transposed B operand of
+  // dV / dK from dO (V waves) or Q (K waves).  Buffer and 16-row chunk
+  // offsets are immediates.  The swizzle permutes the 16-byte chunks of a row
+  // (offset bits 4-7), so A fragment kk sits at roff0 ^ (32 kk): each step
+  // rebuilds these from roff0 (an empty asm hides that they do not change),
+  // which keeps seven registers free.
+  constexpr uint32_t kGOff = kQt * D * 2;  // dO tile after the Q tile
+  const uint32_t roff0 = row_frag_off<D>(lane, 0) + (kwave ? kGOff : 0u);
   uint32_t toff[D / 32][2];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
-    toff[dt][0] = tr_off<D>(lane, dt, 0);
-    toff[dt][1] = tr_off<D>(lane, dt, 1);
+    toff[dt][0] = tr_off<D>(lane, dt, 0) + (kwave ? 0u : kGOff);
+    toff[dt][1] = tr_off<D>(lane, dt, 1) + (kwave ? 0u : kGOff);
   }
+  const char* const tiles_c = reinterpret_cast<const char*>(&tiles[0][0]);
 
   const int wave_key_last = min(kw0 + 31, L - 1);
   const bool wave_has_keys = kw0 < L;
@@ -315,140 +309,198 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     }
   }
 
-  // Prologue: steps 0 and 1 in flight, step 0's side values in LDS.
+  // Steps are software-pipelined.  Tile t (a step's Q and dO rows with their
+  // side values) lives in buffer t % 4.  In step st the V waves compute
+  // dV += P(st)^T dO(st) from the P(st) they made one step earlier, and
+  // S(st+1) -> P(st+1), which they hand to the K waves through LDS; the K
+  // waves compute dP(st) = dO(st) V^T, dS(st) = P(st) (dP(st) - delta) and
+  // dK += dS(st)^T Q(st).  Each step ends with one barrier.  Tile st+3 is
+  // loaded into the buffer tile st-1 left; tile st+2 must have landed by the
+  // step's end.  The loop runs in groups of four steps (buffers and LDS
+  // offsets fixed at compile time, the handed-over P registers alternating);
+  // steps past the last do nothing.
   Cursor cur = nqt2 > 0 ? Cursor{qs2 + (nqt2 - 1) * kQt, 0, qs2, qe2}
-                        : Cursor{qs1 + (nqt1 - 1) * kQt, 0, qs1, qe1};  // step st
-  Cursor nxt = cur;                              // step st + 2
-  float side_next = 0.f, side_new = 0.f;
+                        : Cursor{qs1 + (nqt1 - 1) * kQt, 0, qs1, qe1};  // tile st
+  Cursor nx1 = cur;                                                     // tile st + 1
+  advance(nx1);
+  Cursor ld = cur;                                                      // next tile to load
+  // Prologue: tiles 0-2 issued, 0 and 1 landed.
   if (nsteps > 0) {
-    if (wave == 0) store_side(load_side(nxt), 0);
-    issue_step(nxt, std::integral_constant<int, 0>{});
-    advance(nxt);
+    issue_step(ld, 0);
+    advance(ld);
     if (nsteps > 1) {
-      if (wave == 0) side_next = load_side(nxt);
-      issue_step(nxt, std::integral_constant<int, 1>{});
-      advance(nxt);
+      issue_step(ld, 1);
+      advance(ld);
+    }
+    if (nsteps > 2) {
+      issue_step(ld, 2);
+      advance(ld);
     }
   }
-  if (nsteps > 1) wait_all_but_newest();  // step 0's tile landed (step 1's may remain)
-  else wait_vmem();
-  __syncthreads();
+  // Everything landed, the K/V fragments included: the compiler does not
+  // count the direct loads, so a partial wait here would leave it waiting
+  // for those fragments (and with them every load in flight) inside the loop.
+  wait_vmem();
+  barrier_lds();
 
-  auto step = [&](int st, auto bc) {
-    constexpr int buf = decltype(bc)::value;  // st % 3
-    // Side values first: an LDS read waits for every direct load in flight
-    // into an array the compiler cannot tell apart, so it goes before this
-    // step's loads are issued.  Register r4 group: rows 8 r4 + 4 half + 0..3.
-    f32x4 l2v[4], dlv[4];
+  auto active = [&](const Cursor& c) {
+    return wave_has_keys &&
+           ((c.qt0 < w1hi && c.qt0 + kQt > w1lo) || (c.qt0 < w2hi && c.qt0 + kQt > w2lo));
+  };
+  // Side values of this lane's accumulator rows 8 r4 + 4 half + 0..3 of the
+  // tile in buffer `buf`: LSE * log2(e) (V waves) or delta (K waves).
+  auto read_side = [&](auto bc, int r4) {
+    constexpr int buf = decltype(bc)::value;
+    return *reinterpret_cast<const f32x4*>(&lds.v[buf][kwave ? 1 : 0][8 * r4 + 4 * half]);
+  };
+  // V waves: S = Q K^T of the tile in buffer `buf` (queries on M, keys on N).
+  // K waves: dP = dO V^T of the same tile.
+  auto qk_product = [&](auto bc) {
+    constexpr int buf = decltype(bc)::value;
+    uint32_t r0 = roff0;
+    asm volatile("" : "+v"(r0));
+    f32x16 sc = f32x16{};
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      l2v[r4] = *reinterpret_cast<const f32x4*>(&lds.lse2[buf][8 * r4 + 4 * half]);
-      dlv[r4] = *reinterpret_cast<const f32x4*>(&lds.delta[buf][8 * r4 + 4 * half]);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const bf16x8 a8 = *reinterpret_cast<const bf16x8*>(
+          tiles_c + buf * kTileBytes + (r0 ^ (32u * kk)));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, kvf[kk], sc, 0, 0, 0);
     }
-    if (st + 2 < nsteps) {
-      if (wave == 0) side_new = load_side(nxt);
-      issue_step(nxt, std::integral_constant<int, (buf + 2) % 3>{});
-      advance(nxt);
+    return sc;
+  };
+  // V waves: P = exp2(S scale log2 e - LSE log2 e) over admitted (row, key)
+  // pairs, as bf16 pairs; register r of a lane holds query row 8(r/4) +
+  // 4 half + r%4 of the tile at cursor c.  In a tile not wholly admitted, a
+  // 32-bit row mask of this lane's key selects the pairs.
+  auto make_p = [&](const f32x16& sc, auto bc, const Cursor& c, uint32_t (&pk)[2][4]) {
+    const int qt0 = c.qt0, qe = c.end;
+    const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
+                                          (qt0 >= f2lo && qt0 + kQt <= f2hi));
+    auto rows = [&](bool masked, uint32_t m) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l2v = read_side(bc, r4);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = fast_exp2(fmaf(sc[4 * r4 + e], a.scale_log2, -l2v[e]));
+          v[e] = !masked || ((m >> (8 * r4 + e)) & 1u) ? pv : 0.f;
+        }
+        pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
+        pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
+      }
+    };
+    if (full) {
+      rows(false, 0u);
+    } else {
+      auto bits = [&](int lo, int hi) -> uint64_t {  // rows [lo, hi) of the tile
+        const int x = min(max(lo - qt0, 0), 32), y = min(max(hi - qt0, 0), 32);
+        return ((1ull << y) - 1) & ~((1ull << x) - 1);
+      };
+      const uint32_t m =
+          (uint32_t)((bits(kr.lo, kr.hi) | bits(kr.lo2, kr.hi2)) & bits(qt0, qe));
+      rows(true, m >> (4 * half));
     }
-    const int qt0 = cur.qt0, qe = cur.end;
-    const bool active = wave_has_keys && ((qt0 < w1hi && qt0 + kQt > w1lo) ||
-                                          (qt0 < w2hi && qt0 + kQt > w2lo));
-    // V waves compute S = Q K^T and P (masked, bf16) and hand P to the K wave
-    // of the same 32 keys through LDS; K waves compute dP = dO V^T meanwhile.
-    // After the barrier the V wave accumulates dV += P^T dO and the K wave
-    // forms dS = P (dP - delta) and accumulates dK += dS^T Q (keys on M, dims
-    // on N, queries contracted, the B operand through the transposed read).
-    // Register r of a lane holds query row 8(r/4) + 4 half + r%4.
-    const char* qtile = reinterpret_cast<const char*>(qbuf(bc));
-    const char* gtile = reinterpret_cast<const char*>(gbuf(bc));
-    uint32_t pk[2][4];
-    f32x16 dp = f32x16{};
-    uint32_t* pex = &p_xchg[wave & 3][0];
-    if (active) {
-      if (!kwave) {
-        const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
-                                              (qt0 >= f2lo && qt0 + kQt <= f2hi));
-        f32x16 sc = f32x16{};
+  };
+  // acc += X^T Y over the tile's 32 query rows: X (keys on M, queries on K)
+  // from the P or dS registers, Y (queries on K, dims on N) from the
+  // row-major tile in buffer `buf` (dO or Q) through the transposed read.
+  auto accumulate = [&](const uint32_t (&pk)[2][4], auto bc) {
+    constexpr int buf = decltype(bc)::value;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qtile + roff[kk]);
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kf[kk], sc, 0, 0, 0);
-        }
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int q0r = 8 * r4 + 4 * half;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pv = fast_exp2(fmaf(sc[4 * r4 + e], a.scale_log2, -l2v[r4][e]));
-            if (!full) {
-              const int i = qt0 + q0r + e;
-              const bool ok = (i < qe) & row_sees(kr, i);
-              pv = ok ? pv : 0.f;
-            }
-            v[e] = pv;
-          }
-          pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
-          pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pex[j * 64 + lane] = pk[j >> 2][j & 3];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 ga8 = *reinterpret_cast<const bf16x8*>(gtile + roff[kk]);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga8, vf[kk], dp, 0, 0, 0);
-        }
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const char* bt = tiles_c + buf * kTileBytes + c * 16 * D * 2;
+        const bf16x8 b8 = tr_pair(bt + toff[dt][0], bt + toff[dt][1]);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b8, acc[dt], 0, 0, 0);
       }
     }
-    barrier_lds();  // P of every key quarter is in LDS
-    if (active) {
-      if (kwave) {
+  };
+  uint32_t* const pex = &p_xchg[0][wave & 3][0][lane * 4];
+  constexpr int kPexParity = 4 * 2 * 64 * 4;  // words between the two parities
+  auto put_p = [&](int parity, const uint32_t (&pk)[2][4]) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const uint32_t w0 = pex[((r4 >> 1) * 4 + (r4 & 1) * 2 + 0) * 64 + lane];
-          const uint32_t w1 = pex[((r4 >> 1) * 4 + (r4 & 1) * 2 + 1) * 64 + lane];
-          const float p[4] = {bf16_to_f32(w0 & 0xffffu), bf16_to_f32(w0 >> 16),
-                              bf16_to_f32(w1 & 0xffffu), bf16_to_f32(w1 >> 16)};
-          float v[4];
+    for (int c = 0; c < 2; ++c)
+      *reinterpret_cast<u32x4*>(pex + parity * kPexParity + c * 64 * 4) =
+          u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]};
+  };
+  // P(st+1) (bf16 pairs) handed from a step to the next in V waves.
+  struct Carry {
+    uint32_t w[2][4];
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Pre-step: P(0) (V waves, also handed over through LDS).
+  Carry carry_a = {}, carry_b = {};
+  if (nsteps > 0 && !kwave && active(cur)) {
+    const f32x16 sc = qk_product(I0{});
+    make_p(sc, I0{}, cur, carry_a.w);
+    put_p(0, carry_a.w);
+  }
+  barrier_lds();
+
+  auto step = [&](int st, auto bc, const Carry& cin, Carry& cout) {
+    constexpr int b = decltype(bc)::value;  // st % 4
+    using B1 = std::integral_constant<int, (b + 1) & 3>;
+    if (st + 3 < nsteps) {
+      issue_step(ld, (b + 3) & 3);
+      advance(ld);
+    }
+    const bool act = st < nsteps && active(cur);
+    const bool act1 = st + 1 < nsteps && active(nx1);
+    // V waves: S(st+1), then dV += P(st)^T dO(st), then P(st+1) (its
+    // exponentials overlap the dV products).  K waves: dP(st), dS(st) =
+    // P(st) (dP(st) - delta), then dK += dS(st)^T Q(st).  One accumulate
+    // for both roles keeps the accumulators in one set of registers.
+    f32x16 sc;  // S(st+1) or dP(st)
+    uint32_t xw[2][4];
+    if (!kwave) {
+      if (act1) sc = qk_product(B1{});
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = p[e] * (dp[4 * r4 + e] - dlv[r4][e]);
-          pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
-          pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
-        }
+      for (int j = 0; j < 8; ++j) xw[j >> 2][j & 3] = cin.w[j >> 2][j & 3];
+    } else if (act) {
+      u32x4 pw[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        pw[c] = *reinterpret_cast<const u32x4*>(pex + (b & 1) * kPexParity + c * 64 * 4);
+      sc = qk_product(bc);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 dlv = read_side(bc, r4);
+        const uint32_t w0 = pw[r4 >> 1][(r4 & 1) * 2 + 0];
+        const uint32_t w1 = pw[r4 >> 1][(r4 & 1) * 2 + 1];
+        const float p[4] = {bf16_to_f32(w0 & 0xffffu), bf16_to_f32(w0 >> 16),
+                            bf16_to_f32(w1 & 0xffffu), bf16_to_f32(w1 >> 16)};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = p[e] * (sc[4 * r4 + e] - dlv[e]);
+        xw[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
+        xw[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
       }
-      const char* btile = kwave ? qtile : gtile;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16x8 b8 = tr_pair(btile + toff[dt][0] + c * 16 * D * 2,
-                                    btile + toff[dt][1] + c * 16 * D * 2);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b8, acc[dt], 0, 0, 0);
-        }
-      }
+    }
+    if (act) accumulate(xw, bc);
+    if (!kwave && act1) {
+      make_p(sc, B1{}, nx1, cout.w);
+      put_p((b + 1) & 1, cout.w);
     }
     advance(cur);
-    // Step st+1's tile must have landed; step st+2's stays in flight across
-    // the barrier.
-    constexpr int buf1 = (buf + 1) % 3;
-    if (st + 2 < nsteps) {
-      if (wave == 0) {
-        store_side(side_next, buf1);
-        side_next = side_new;
-      }
-      wait_all_but_newest();
-    } else {
-      if (wave == 0 && st + 1 < nsteps) store_side(side_next, buf1);
-      wait_vmem();
-    }
+    advance(nx1);
+    // Tile st+2 must have landed; tile st+3 stays in flight across the
+    // barrier.
+    if (st + 3 < nsteps) wait_all_but_newest();
+    else wait_vmem();
     barrier_lds();
   };
-  for (int st = 0; st < nsteps; st += 3) {
-    step(st, std::integral_constant<int, 0>{});
-    if (st + 1 < nsteps) step(st + 1, std::integral_constant<int, 1>{});
-    if (st + 2 < nsteps) step(st + 2, std::integral_constant<int, 2>{});
+  for (int st = 0; st < nsteps; st += 4) {
+    step(st, I0{}, carry_a, carry_b);
+    step(st + 1, I1{}, carry_b, carry_a);
+    step(st + 2, I2{}, carry_a, carry_b);
+    step(st + 3, I3{}, carry_b, carry_a);
   }
 
   // Epilogue: lane holds dims 32 dt + lane%32 of keys 8(r/4) + 4 half + r%4.

@@ -172,8 +172,8 @@ bca_status_t bca_fwd(const void* q, const void* k, const void* v, void* o, float
 
 size_t bca_staircase_bwd_workspace(int32_t total, int32_t hq, int32_t hkv, int32_t d) {
   if (total < 0 || hq <= 0 || hkv <= 0 || d <= 0) return 0;
-  const size_t delta = (size_t)hq * total * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  const size_t rows = (((size_t)hq * total * sizeof(float)) + 255) & ~(size_t)255;
+  return 2 * rows;  // delta, then LSE * log2(e)
 }
 
 }  // extern "C"
@@ -210,6 +210,7 @@ static bca_status_t bwd_impl(const void* q, const void* k, const void* v, const 
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
   a.cu_seqlens = cu_seqlens;
   a.s_copies = s_copies;
   a.group_start = group_start;

@@ -54,6 +54,51 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, as_lds(lds_base), 16, voffset, 0, 0, 0);
 }
 
+// The same descriptor as four words, for inline assembly.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)nbytes, 0x00020000};
+}
+
+// Direct-to-LDS loads written as inline assembly: from buffer `r` at
+// voffset into LDS at byte address lds_addr + W * lane, W = 16 bytes
+// (buffer_load_lds16_asm) or 4 bytes (buffer_load_lds4_asm).  The compiler
+// does not know these write LDS, so it adds no wait for them before later
+// LDS reads, and counts them in none of its own vmcnt waits (which can
+// only grow stricter by it): the caller orders the data with explicit vmcnt
+// waits and barriers.  M0 is written here and nowhere else in the kernels
+// that use these (the compiler reserves it, so it is listed only for the
+// reader).  The nops cover the write-to-use distances of the descriptor
+// SGPRs (when the compiler builds them with a VALU op) and of M0.
+__device__ __forceinline__ void buffer_load_lds16_asm(i32x4 r, uint32_t lds_addr,
+                                                      uint32_t voffset) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void buffer_load_lds4_asm(i32x4 r, uint32_t lds_addr,
+                                                     uint32_t voffset) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(r)
+      : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)(p));
+}
+
 // Wait until this wave's outstanding vector-memory operations (including
 // direct-to-LDS loads) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

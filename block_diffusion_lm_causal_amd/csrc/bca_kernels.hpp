@@ -69,6 +69,7 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* delta;       // [hq, total] float32 workspace: rowsum(dO * O)
+  float* lse2;        // [hq, total] float32 workspace: LSE * log2(e)
   const int32_t* cu_seqlens;
   const int32_t* s_copies;
   const int32_t* group_start;

@@ -115,8 +115,9 @@ bca_status_t bca_staircase_fwd(const void* q, const void* k, const void* v, void
                                int32_t hkv, int32_t d, int32_t block_size, float scale,
                                bca_dtype_t dtype, void* stream);
 
-/* Bytes of workspace bca_staircase_bwd needs: the float32 row terms
- * rowsum(dO * O), [hq, total] (rounded up to 256 bytes). */
+/* Bytes of workspace bca_staircase_bwd needs: two float32 arrays of row
+ * terms, [hq, total] each (each rounded up to 256 bytes): rowsum(dO * O) and
+ * LSE * log2(e). */
 size_t bca_staircase_bwd_workspace(int32_t total, int32_t hq, int32_t hkv, int32_t d);
 
 /*
