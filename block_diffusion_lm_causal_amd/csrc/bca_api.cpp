@@ -94,7 +94,7 @@ static bca_status_t fwd_impl(const void* q, const void* k, const void* v, void* 
     return fail(BCA_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == BCA_BF16) {
-    bca::FwdArgs a;
+    bca::FwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -115,7 +115,7 @@ static bca_status_t fwd_impl(const void* q, const void* k, const void* v, void* 
     a.scale_log2 = scale * kLog2e;
     return hip_status(bca::launch_fwd_bf16(a, max_seqlen, s), "forward launch");
   }
-  bca::FwdF32Args a;
+  bca::FwdF32Args a{};
   a.q = static_cast<const float*>(q);
   a.k = static_cast<const float*>(k);
   a.v = static_cast<const float*>(v);
@@ -199,7 +199,7 @@ static bca_status_t bwd_impl(const void* q, const void* k, const void* v, const 
   if (!workspace || ws_bytes < need)
     return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (!aligned16(workspace)) return fail(BCA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  bca::BwdArgs a;
+  bca::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -357,7 +357,7 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
                         float scale, bca_dtype_t dtype, int32_t num_splits, void* workspace,
                         size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
-  bca::DecodeArgs a;
+  bca::DecodeArgs a{};
   const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
                                       num_splits, workspace, ws_bytes, &a);
   if (st != BCA_OK) return st;
@@ -371,7 +371,7 @@ bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float
   g_last_error[0] = '\0';
   if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f)
     return fail(BCA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
-  bca::DecodeArgs a;
+  bca::DecodeArgs a{};
   const bca_status_t st = decode_args(q, k8, v8, o, lse, q_len, kv_len, hq, hkv, d, scale,
                                       BCA_BF16, num_splits, workspace, ws_bytes, &a);
   if (st != BCA_OK) return st;
@@ -394,7 +394,7 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
   *graph = nullptr;
   if (steps < 1 || steps > kMaxGraphSteps)
     return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
-  bca::DecodeArgs a;
+  bca::DecodeArgs a{};
   const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
                                       num_splits, workspace, ws_bytes, &a);
   if (st != BCA_OK) return st;
