@@ -68,11 +68,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 }
 
-// s_waitcnt vmcnt(n) for small n (expcnt and lgkmcnt left unconstrained).
+// s_waitcnt vmcnt(n), n < 64 (expcnt and lgkmcnt left unconstrained; the
+// two high bits of vmcnt sit at bits 14-15 of the immediate).
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // A operand fragment of a row-major swizzled tile: row lane%32 (+ row_base),

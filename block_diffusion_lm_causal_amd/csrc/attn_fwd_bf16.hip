@@ -279,6 +279,12 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
     ws.l = lsum;
     rescale_prev = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_prev = alpha;
+    // P must be complete within this phase: the compiler would otherwise move
+    // the exponentials past the barrier, next to the P V product that uses
+    // them, which puts this group's VALU work into its own MFMA phase.
+#pragma unroll
+    for (int c = 0; c < kBN / 16; ++c)
+      asm volatile("" ::"v"(pk[c][0]), "v"(pk[c][1]), "v"(pk[c][2]), "v"(pk[c][3]), "v"(lsum));
   };
 
   // Group A's loads in phase 2t: K(t+1) and V(t).
