@@ -75,10 +75,11 @@ __device__ __forceinline__ void pv_update(const char* vt, const uint32_t (&voff)
 //   A: MFMA(t), then softmax(t);   B: softmax(t-1), then MFMA(t).
 // Each group runs its own straight-line loop (two barriers per iteration, so
 // both groups pass the same barriers), which keeps S and P in fixed registers.
-// Only group A loads K/V: in phase 2t, after its own LDS reads, it issues
-// K(t+1) and V(t) into the buffers last read in phase 2t-1 (double buffers),
-// and waits for them at the end of phase 2t+1.  Group B never has a tile
-// load in flight, so none of its LDS reads waits on one.
+// Each group loads at the start of its softmax phase, where the issue (a few
+// hundred cycles of the address unit) does not lengthen an MFMA phase: B
+// issues V(t) in phase 2t, A issues K(t+1) in phase 2t+1, into the buffers
+// last read in phase 2t-1 (double buffers), and each waits for its own loads
+// at the end of phase 2t+1.
 
 
 template <int D>
@@ -248,18 +249,19 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
         }
       }
     }
-    float mt[kBN / 4];
+    // Row max of the lane's 32 scores: four independent chains of
+    // three-input maxima (v_max3_f32), 18 instructions.
+    float mc[4];
 #pragma unroll
-    for (int h = 0; h < kBN / 32; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mt[h * 8 + r / 2] = fmaxf(s[h][r], s[h][r + 1]);
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& v = s[c >> 1];
+      const int o = (c & 1) * 8;
+      float m = fmaxf(fmaxf(v[o + 0], v[o + 1]), v[o + 2]);
+      m = fmaxf(fmaxf(m, v[o + 3]), v[o + 4]);
+      m = fmaxf(fmaxf(m, v[o + 5]), v[o + 6]);
+      mc[c] = fmaxf(m, v[o + 7]);
     }
-#pragma unroll
-    for (int w = kBN / 8; w >= 1; w >>= 1) {
-#pragma unroll
-      for (int i = 0; i < w; ++i) mt[i] = fmaxf(mt[i], mt[i + w]);
-    }
-    const float mloc = xhalf_max(mt[0]) * scale_log2;
+    const float mloc = xhalf_max(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]))) * scale_log2;
     const bool grow = mloc > ws.m + kRescaleSlack;
     const float m_new = grow ? mloc : ws.m;
     const float alpha = fast_exp2(ws.m - m_new);
@@ -287,25 +289,30 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
       asm volatile("" ::"v"(pk[c][0]), "v"(pk[c][1]), "v"(pk[c][2]), "v"(pk[c][3]), "v"(lsum));
   };
 
-  // Group A's loads in phase 2t: K(t+1) and V(t).
-  auto issue = [&](int t) {
-    if (t + 1 < ntile) ld.issue(p.k, kv_stride, tile_k0(t + 1), tile_end(t + 1), lds.k[(t + 1) & 1]);
+  // Loads, each at the start of its group's softmax phase, where the issue
+  // (a few hundred cycles of the address unit) does not lengthen an MFMA
+  // phase: group B issues V(t) in phase 2t, group A K(t+1) in phase 2t+1.
+  // Both go into buffers last read in phase 2t-1 and are waited for (vmcnt)
+  // by their issuer at the end of phase 2t+1, before phase 2t+2 reads them.
+  auto issue_k = [&](int t) {
+    if (t < ntile) ld.issue(p.k, kv_stride, tile_k0(t), tile_end(t), lds.k[t & 1]);
+  };
+  auto issue_v = [&](int t) {
     if (t < ntile) ld.issue(p.v, kv_stride, tile_k0(t), tile_end(t), lds.v[t & 1]);
   };
 
-  // Phase barriers are barrier_lds(): the loads issued in phase 2t stay in
-  // flight across the barrier that ends it and are waited for (vmcnt) only at
-  // the end of phase 2t+1.
+  // Phase barriers are barrier_lds(), except the one ending phase 2t+1,
+  // which first waits (vmcnt) for the loads of the iteration.
   if (grp == 0) {
     mfma_phase(0, false, true);
-    issue(0);
     barrier_lds();
+    issue_k(1);
     softmax_phase(0);
     wait_vmem_barrier();
     for (int t = 1; t < ntile; ++t) {
       mfma_phase(t, true, true);
-      issue(t);
       barrier_lds();
+      issue_k(t + 1);
       softmax_phase(t);
       wait_vmem_barrier();
     }
@@ -313,14 +320,16 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
     barrier_lds();
     barrier_lds();
   } else {
+    issue_v(0);
     barrier_lds();
     mfma_phase(0, false, true);
-    barrier_lds();
+    wait_vmem_barrier();
     for (int t = 1; t < ntile; ++t) {
+      issue_v(t);
       softmax_phase(t - 1);
       barrier_lds();
       mfma_phase(t, true, true);
-      barrier_lds();
+      wait_vmem_barrier();
     }
     softmax_phase(ntile - 1);
     barrier_lds();
