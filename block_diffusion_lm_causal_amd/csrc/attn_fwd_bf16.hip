@@ -190,14 +190,63 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
   bool rescale_prev = false;
 
   // MFMA phase: the rescale pending from the previous softmax, O^T += V^T P^T
-  // of tile t-1 (t >= 1), then S^T of tile t (t < ntile).
+  // of tile t-1 (t >= 1) and S^T of tile t (t < ntile).  With both products
+  // the MFMAs alternate (P V, S, P V, S, ...), so the two transposed V reads
+  // of one and the K read of the other spread evenly over the phase instead
+  // of the 32 V reads crowding the LDS at its start.
   auto mfma_phase = [&](int t, bool do_pv, bool do_s) {
     if (rescale_prev) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
     }
-    if (do_pv) pv_update<D>(reinterpret_cast<const char*>(lds.v[(t - 1) & 1]), voff, pk, ws);
-    if (do_s) {
+    if (do_pv && do_s) {
+      const char* vt = reinterpret_cast<const char*>(lds.v[(t - 1) & 1]);
+      const char* kt = reinterpret_cast<const char*>(lds.k[t & 1]);
+      constexpr int kN = kBN * D / 512;  // MFMAs of each product per tile
+      constexpr int kAh = 2;             // MFMA pairs whose operands are read ahead
+      auto vfrag = [&](int i) {
+        const int c = i / (D / 32), dt = i % (D / 32);
+        const s16x4 lo = lds_read_tr16(vt + voff[dt][0] + c * 16 * D * 2);
+        const s16x4 hi = lds_read_tr16(vt + voff[dt][1] + c * 16 * D * 2);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+      };
+      auto kfrag = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(kt + koff[i / 2] + (i % 2) * 32 * D * 2);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 va[kAh], kb[kAh];
+#pragma unroll
+      for (int i = 0; i < kAh; ++i) {
+        va[i] = vfrag(i);
+        kb[i] = kfrag(i);
+      }
+#pragma unroll
+      for (int h = 0; h < kBN / 32; ++h) s[h] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int c = i / (D / 32), dt = i % (D / 32);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
+        ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kAh], pb, ws.acc[dt], 0, 0, 0);
+        s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[i % kAh], qf[i / 2], s[i % 2], 0, 0, 0);
+        if (i + kAh < kN) {
+          va[i % kAh] = vfrag(i + kAh);
+          kb[i % kAh] = kfrag(i + kAh);
+        }
+      }
+      // issue order: the reads of kAh pairs, then (2 MFMAs, 3 reads) groups,
+      // then the last MFMAs (group masks: 0x100 LDS read, 0x008 MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAh, 0);
+#pragma unroll
+      for (int i = 0; i < kN - kAh; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAh, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else if (do_pv) {
+      pv_update<D>(reinterpret_cast<const char*>(lds.v[(t - 1) & 1]), voff, pk, ws);
+    } else if (do_s) {
       // K fragments (kk, h) in order i = 2 kk + h, read kAhead ahead of use
       // so that LDS latency hides behind the MFMAs; the scheduling groups
       // below pin that order (left alone, the scheduler reads only two ahead).
