@@ -193,15 +193,16 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
   // of tile t-1 (t >= 1) and S^T of tile t (t < ntile).  With both products
   // the MFMAs alternate (P V, S, P V, S, ...), so the two transposed V reads
   // of one and the K read of the other spread evenly over the phase instead
-  // of the 32 V reads crowding the LDS at its start.
-  auto mfma_phase = [&](int t, bool do_pv, bool do_s) {
+  // of the 32 V reads crowding the LDS at its start.  par = t & 1 selects the
+  // buffers: K(t) in k[par], V(t-1) in v[par ^ 1].
+  auto mfma_phase = [&](int t, bool do_pv, bool do_s, int par) {
     if (rescale_prev) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] *= alpha_prev;
     }
     if (do_pv && do_s) {
-      const char* vt = reinterpret_cast<const char*>(lds.v[(t - 1) & 1]);
-      const char* kt = reinterpret_cast<const char*>(lds.k[t & 1]);
+      const char* vt = reinterpret_cast<const char*>(lds.v[par ^ 1]);
+      const char* kt = reinterpret_cast<const char*>(lds.k[par]);
       constexpr int kN = kBN * D / 512;  // MFMAs of each product per tile
       constexpr int kAh = 2;             // MFMA pairs whose operands are read ahead
       auto vfrag = [&](int i) {
@@ -245,12 +246,12 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAh, 0);
       __builtin_amdgcn_sched_barrier(0);
     } else if (do_pv) {
-      pv_update<D>(reinterpret_cast<const char*>(lds.v[(t - 1) & 1]), voff, pk, ws);
+      pv_update<D>(reinterpret_cast<const char*>(lds.v[par ^ 1]), voff, pk, ws);
     } else if (do_s) {
       // K fragments (kk, h) in order i = 2 kk + h, read kAhead ahead of use
       // so that LDS latency hides behind the MFMAs; the scheduling groups
       // below pin that order (left alone, the scheduler reads only two ahead).
-      const char* kt = reinterpret_cast<const char*>(lds.k[t & 1]);
+      const char* kt = reinterpret_cast<const char*>(lds.k[par]);
       constexpr int kFrags = (D / 16) * (kBN / 32);
       constexpr int kAhead = 4;
       auto frag = [&](int i) {
@@ -352,37 +353,52 @@ __device__ __forceinline__ void attend_pp(const WgPlan& p, int q_stride, int kv_
 
   // Phase barriers are barrier_lds(), except the one ending phase 2t+1,
   // which first waits (vmcnt) for the loads of the iteration.
+  // The loops are unrolled by two, so the parity of t -- which LDS buffer
+  // each phase reads -- is a constant in the code, and every LDS address is
+  // a lane offset plus an immediate.
   if (grp == 0) {
-    mfma_phase(0, false, true);
-    barrier_lds();
-    issue_k(1);
-    softmax_phase(0);
-    wait_vmem_barrier();
-    for (int t = 1; t < ntile; ++t) {
-      mfma_phase(t, true, true);
+    auto step = [&](int t, int par) {
+      mfma_phase(t, true, true, par);
       barrier_lds();
       issue_k(t + 1);
       softmax_phase(t);
       wait_vmem_barrier();
+    };
+    mfma_phase(0, false, true, 0);
+    barrier_lds();
+    issue_k(1);
+    softmax_phase(0);
+    wait_vmem_barrier();
+    int t = 1;
+    for (; t + 1 < ntile; t += 2) {
+      step(t, 1);
+      step(t + 1, 0);
     }
-    mfma_phase(ntile, true, false);
+    if (t < ntile) step(t, 1);
+    mfma_phase(ntile, true, false, ntile & 1);
     barrier_lds();
     barrier_lds();
   } else {
-    issue_v(0);
-    barrier_lds();
-    mfma_phase(0, false, true);
-    wait_vmem_barrier();
-    for (int t = 1; t < ntile; ++t) {
+    auto step = [&](int t, int par) {
       issue_v(t);
       softmax_phase(t - 1);
       barrier_lds();
-      mfma_phase(t, true, true);
+      mfma_phase(t, true, true, par);
       wait_vmem_barrier();
+    };
+    issue_v(0);
+    barrier_lds();
+    mfma_phase(0, false, true, 0);
+    wait_vmem_barrier();
+    int t = 1;
+    for (; t + 1 < ntile; t += 2) {
+      step(t, 1);
+      step(t + 1, 0);
     }
+    if (t < ntile) step(t, 1);
     softmax_phase(ntile - 1);
     barrier_lds();
-    mfma_phase(ntile, true, false);
+    mfma_phase(ntile, true, false, ntile & 1);
     barrier_lds();
   }
 }
