@@ -526,8 +526,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 
 template <int D>
 struct DqLds {
-  uint16_t k[3][kBN * D];
-  uint16_t v[2][kBN * D];
+  uint16_t k[4][kBN * D];  // K(t) in k[t & 3]
+  uint16_t v[2][kBN * D];  // V(t) in v[t & 1]
 };
 
 template <int D>
@@ -641,50 +641,91 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
     wait_vmem();
     __syncthreads();
     f32x16 s[kBN / 32], dp[kBN / 32];
-    uint32_t pk[kBN / 16][4];  // dS^T of the tile between its VALU and dQ phases
-    // MFMA phase: dQ^T += K^T dS^T of tile t-1 (t >= 1), then S^T and dP^T of
-    // tile t (t < ntile).
-    auto mfma_phase = [&](int t, bool do_dq, bool do_s) {
-      if (do_dq) {
-        const char* kt = reinterpret_cast<const char*>(lds.k[(t - 1) % 3]);
+    // dS^T of the tile between its VALU and dQ phases; zero before the first
+    uint32_t pk[kBN / 16][4] = {};
+    // MFMA phase t: dQ^T += K^T dS^T of tile t-1 and S^T, dP^T of tile t.
+    // Every phase runs the same straight-line code (a second code path
+    // pushes the kernel past its register budget): in phase 0 the dQ^T
+    // MFMAs add K^T times the zero dS^T (K of tile 0, finite), and in phase
+    // ntile the S^T and dP^T of stale tile memory are computed and dropped.
+    // The MFMAs run dQ^T first (dS^T(t-1) is dead before S^T(t) and dP^T(t)
+    // are live), then S^T and dP^T alternating; the LDS operands of each
+    // MFMA (two transposed K reads for dQ^T, one K or V read otherwise) are
+    // read kAh MFMAs ahead, so LDS latency hides behind the MFMAs between.
+    auto mfma_phase = [&](int kti, int kdi, int vti) {
+      const char* kd = reinterpret_cast<const char*>(lds.k[kdi]);
+      const char* kt = reinterpret_cast<const char*>(lds.k[kti]);
+      const char* vt = reinterpret_cast<const char*>(lds.v[vti]);
+      constexpr int kN = D / 16;   // dQ^T MFMAs = S^T MFMAs = dP^T MFMAs
+      constexpr int kM = 3 * kN;   // MFMAs of the phase
+      constexpr int kAh = 3;
+      static_assert(kBN == 32, "one S^T / dP^T accumulator per tile");
+      static_assert(kAh <= kN, "lookahead within the dQ^T MFMAs");
+      // MFMA m: m < kN is dQ^T MFMA m (c = m / (D/32), dt = m % (D/32)),
+      // then S^T and dP^T alternate over kk = (m - kN) / 2.
+      auto frag = [&](int m) {
+        if (m < kN) {
+          const int c = m / (D / 32), dt = m % (D / 32);
+          return tr_pair(kd + toff[dt][0] + c * 16 * D * 2, kd + toff[dt][1] + c * 16 * D * 2);
+        }
+        const int kk = (m - kN) / 2;
+        return *reinterpret_cast<const bf16x8*>(((m - kN) % 2 ? vt : kt) + koff[kk]);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 fr[kAh];
 #pragma unroll
-        for (int c = 0; c < kBN / 16; ++c) {
+      for (int m = 0; m < kAh; ++m) fr[m] = frag(m);
+      s[0] = f32x16{};
+      dp[0] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        if (m < kN) {
+          const int c = m / (D / 32), dt = m % (D / 32);
           const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const bf16x8 ka = tr_pair(kt + toff[dt][0] + c * 16 * D * 2,
-                                      kt + toff[dt][1] + c * 16 * D * 2);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, db, acc[dt], 0, 0, 0);
-          }
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % kAh], db, acc[dt], 0, 0, 0);
+        } else if ((m - kN) % 2 == 0) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % kAh], qf[(m - kN) / 2], s[0], 0, 0, 0);
+        } else {
+          dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % kAh], gf[(m - kN) / 2], dp[0], 0, 0, 0);
         }
+        if (m + kAh < kM) fr[m % kAh] = frag(m + kAh);
       }
-      if (do_s) {
-        const char* kt = reinterpret_cast<const char*>(lds.k[t % 3]);
-        const char* vt = reinterpret_cast<const char*>(lds.v[t & 1]);
+      // issue order: the reads of the first kAh MFMAs (two per dQ^T MFMA),
+      // then each MFMA followed by the reads of the MFMA kAh later (group
+      // masks: 0x100 LDS read, 0x008 MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAh, 0);
 #pragma unroll
-        for (int h = 0; h < kBN / 32; ++h) {
-          s[h] = f32x16{};
-          dp[h] = f32x16{};
-        }
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-          for (int h = 0; h < kBN / 32; ++h) {
-            const uint32_t off = koff[kk] + h * 32 * D * 2;
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + off);
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + off);
-            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[h], 0, 0, 0);
-            dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[kk], dp[h], 0, 0, 0);
-          }
-        }
+      for (int m = 0; m < kN - kAh; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+#pragma unroll
+      for (int m = kN - kAh; m < kM - kAh; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAh, 0);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // VALU phase of tile t: P^T and dS^T.
+    // VALU phase of tile t: P^T and dS^T.  Masked scores are set to -inf
+    // first (only in tiles not wholly admitted for the wave), so that the
+    // loop below is straight-line code: P = 0 there, and with it dS.
     auto valu_phase = [&](int t) {
       const int k0 = tile_k0(t), kend = tile_end(t);
       const bool full = wave_active && (k0 + kBN <= kend) &&
                         ((k0 + kBN <= e1_all) ||
                          (one_copy && k0 >= rkA.s2 && k0 + kBN <= rkA.e2));
+      if (!full) {
+#pragma unroll
+        for (int h = 0; h < kBN / 32; ++h) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = k0 + h * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
+            s[h][r] = ok ? s[h][r] : kNegInf;
+          }
+        }
+      }
 #pragma unroll
       for (int h = 0; h < kBN / 32; ++h) {
 #pragma unroll
@@ -692,12 +733,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
           float dsv[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            float p = fast_exp2(fmaf(s[h][r + e], a.scale_log2, -lse2));
-            if (!full) {
-              const int j = k0 + h * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-              const bool ok = (j < kend) & ((j < rk.e1) | ((j >= rk.s2) & (j < rk.e2)));
-              p = ok ? p : 0.f;
-            }
+            const float p = fast_exp2(fmaf(s[h][r + e], a.scale_log2, -lse2));
             dsv[e] = p * (dp[h][r + e] - dl);
           }
           pk[h * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(dsv[0], dsv[1]);
@@ -709,28 +745,45 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
     // the end of phase 2t+1.
     auto issue_next = [&](int t) {
       if (t + 1 < ntile) {
-        issue(kb, t + 1, lds.k[(t + 1) % 3]);
+        issue(kb, t + 1, lds.k[(t + 1) & 3]);
         issue(vb, t + 1, lds.v[(t + 1) & 1]);
       }
     };
     // Two groups one phase apart, each in its own straight-line loop (as the
     // forward): A runs MFMA(t) then VALU(t), B runs VALU(t-1) then MFMA(t);
-    // every iteration passes two barriers in both groups.
+    // every iteration passes two barriers in both groups.  The loops are
+    // unrolled by four, so the buffers each phase reads -- K(t) in k[t & 3],
+    // K(t-1) in k[(t-1) & 3], V(t) in v[t & 1] -- are constants in the code
+    // and every LDS address is a lane offset plus an immediate; phase 0
+    // takes its dQ^T operand from k[0] (tile 0; dS^T is zero there).
+    auto phase_a = [&](int t, int kti, int kdi, int vti) {
+      mfma_phase(kti, kdi, vti);
+      issue_next(t);
+      barrier_lds();
+      if (t < ntile) valu_phase(t);
+      wait_vmem_barrier();
+    };
+    auto phase_b = [&](int t, int kti, int kdi, int vti) {
+      if (t >= 1) valu_phase(t - 1);
+      barrier_lds();
+      mfma_phase(kti, kdi, vti);
+      barrier_lds();
+    };
+    auto run = [&](auto&& phase) {
+      phase(0, 0, 0, 0);
+      int t = 1;
+      for (; t + 3 <= ntile; t += 4) {
+        phase(t, 1, 0, 1);
+        phase(t + 1, 2, 1, 0);
+        phase(t + 2, 3, 2, 1);
+        phase(t + 3, 0, 3, 0);
+      }
+      for (; t <= ntile; ++t) phase(t, t & 3, (t - 1) & 3, t & 1);
+    };
     if (grp == 0) {
-      for (int t = 0; t <= ntile; ++t) {
-        mfma_phase(t, t >= 1, t < ntile);
-        issue_next(t);
-        barrier_lds();
-        if (t < ntile) valu_phase(t);
-        wait_vmem_barrier();
-      }
+      run(phase_a);
     } else {
-      for (int t = 0; t <= ntile; ++t) {
-        if (t >= 1) valu_phase(t - 1);
-        barrier_lds();
-        mfma_phase(t, t >= 1, t < ntile);
-        barrier_lds();
-      }
+      run(phase_b);
     }
   }
 
