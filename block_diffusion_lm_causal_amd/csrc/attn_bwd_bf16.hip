@@ -360,13 +360,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     constexpr int buf = decltype(bc)::value;
     uint32_t r0 = roff0;
     asm volatile("" : "+v"(r0));
+    auto frag = [&](int kk) {
+      return *reinterpret_cast<const bf16x8*>(tiles_c + buf * kTileBytes + (r0 ^ (32u * kk)));
+    };
+    // fragments read kQA MFMAs ahead of use, so that LDS latency hides
+    // behind the MFMAs between; the scheduling groups below pin that order
+    // (left alone, the compiler reads one ahead)
+    constexpr int kQA = 4;
+    constexpr int kK = D / 16;
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 fr[kQA];
+#pragma unroll
+    for (int i = 0; i < kQA; ++i) fr[i] = frag(i);
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 a8 = *reinterpret_cast<const bf16x8*>(
-          tiles_c + buf * kTileBytes + (r0 ^ (32u * kk)));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, kvf[kk], sc, 0, 0, 0);
+    for (int kk = 0; kk < kK; ++kk) {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk % kQA], kvf[kk], sc, 0, 0, 0);
+      if (kk + kQA < kK) fr[kk % kQA] = frag(kk + kQA);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, kQA, 0);
+#pragma unroll
+    for (int i = 0; i < kK - kQA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kQA, 0);
+    __builtin_amdgcn_sched_barrier(0);
     return sc;
   };
   // V waves: P = exp2(S scale log2 e - LSE log2 e) over admitted (row, key)
@@ -408,16 +427,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   // row-major tile in buffer `buf` (dO or Q) through the transposed read.
   auto accumulate = [&](const uint32_t (&pk)[2][4], auto bc) {
     constexpr int buf = decltype(bc)::value;
+    constexpr int kM = 2 * (D / 32);  // MFMA m: c = m / (D/32), dt = m % (D/32)
+    constexpr int kAA = 3;        // B operands read kAA MFMAs ahead
+    auto frag = [&](int m) {
+      const char* bt = tiles_c + buf * kTileBytes + (m / (D / 32)) * 16 * D * 2;
+      return tr_pair(bt + toff[m % (D / 32)][0], bt + toff[m % (D / 32)][1]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 fr[kAA];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int i = 0; i < kAA; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const int c = m / (D / 32), dt = m % (D / 32);
       const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const char* bt = tiles_c + buf * kTileBytes + c * 16 * D * 2;
-        const bf16x8 b8 = tr_pair(bt + toff[dt][0], bt + toff[dt][1]);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, b8, acc[dt], 0, 0, 0);
-      }
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, fr[m % kAA], acc[dt], 0, 0, 0);
+      if (m + kAA < kM) fr[m % kAA] = frag(m + kAA);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAA, 0);
+#pragma unroll
+    for (int i = 0; i < kM - kAA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAA, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
   uint32_t* const pex = &p_xchg[0][wave & 3][0][lane * 4];
   constexpr int kPexParity = 4 * 2 * 64 * 4;  // words between the two parities
@@ -448,10 +482,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   auto step = [&](int st, auto bc, const Carry& cin, Carry& cout) {
     constexpr int b = decltype(bc)::value;  // st % 4
     using B1 = std::integral_constant<int, (b + 1) & 3>;
-    if (st + 3 < nsteps) {
-      issue_step(ld, (b + 3) & 3);
-      advance(ld);
-    }
+    // Loads of tile st+3 into the buffer tile st-1 left, issued behind the
+    // first MFMAs of the step so that their issue overlaps the MFMA pipe.
+    auto issue = [&]() {
+      if (st + 3 < nsteps) {
+        issue_step(ld, (b + 3) & 3);
+        advance(ld);
+      }
+    };
     const bool act = st < nsteps && active(cur);
     const bool act1 = st + 1 < nsteps && active(nx1);
     // V waves: S(st+1), then dV += P(st)^T dO(st), then P(st+1) (its
@@ -462,6 +500,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     uint32_t xw[2][4];
     if (!kwave) {
       if (act1) sc = qk_product(B1{});
+      issue();
 #pragma unroll
       for (int j = 0; j < 8; ++j) xw[j >> 2][j & 3] = cin.w[j >> 2][j & 3];
     } else if (act) {
@@ -470,6 +509,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       for (int c = 0; c < 2; ++c)
         pw[c] = *reinterpret_cast<const u32x4*>(pex + (b & 1) * kPexParity + c * 64 * 4);
       sc = qk_product(bc);
+      issue();
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 dlv = read_side(bc, r4);
@@ -483,6 +523,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
         xw[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
         xw[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
       }
+    } else {
+      issue();
     }
     if (act) accumulate(xw, bc);
     if (!kwave && act1) {
