@@ -1,0 +1,55 @@
+"""Host logic of bench.py (no GPU): the source digest that gates the stored
+HBM-traffic figure, the parsing of the committed counter summary, and the
+single-GPU guard."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_digest_is_stable_and_tracks_every_source(tmp_path, monkeypatch):
+    for name in bench.FWD_SOURCES:
+        (tmp_path / name).write_text(f"// {name}\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    d0 = bench.source_digest()
+    assert d0 == bench.source_digest()
+    assert len(d0) == 16 and all(c in "0123456789abcdef" for c in d0)
+    for name in bench.FWD_SOURCES:
+        p = tmp_path / name
+        old = p.read_text()
+        p.write_text(old + " ")
+        assert bench.source_digest() != d0, name
+        p.write_text(old)
+    assert bench.source_digest() == d0
+
+
+def test_stored_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
+    digest = bench.source_digest()
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.stored_traffic("k") is None  # no summary
+    (tmp_path / "k_pmc.md").write_text(f"source_digest: {digest}\nhbm_bytes_per_launch: 12345\n")
+    assert bench.stored_traffic("k") == 12345.0
+    (tmp_path / "k_pmc.md").write_text("source_digest: 0000000000000000\nhbm_bytes_per_launch: 12345\n")
+    assert bench.stored_traffic("k") is None  # counters of another kernel version
+    (tmp_path / "k_pmc.md").write_text(f"source_digest: {digest}\n")
+    assert bench.stored_traffic("k") is None  # no figure
+
+
+def test_committed_counter_summary_parses():
+    text = open(os.path.join(bench.PROFILES, "fwd_bf16_prefill_L4096_pmc.md")).read()
+    assert "FETCH_SIZE" in text and "WRITE_SIZE" in text
+    t = bench.stored_traffic("fwd_bf16_prefill_L4096")
+    # None once the kernel has changed since the counters were taken
+    assert t is None or t > 84_410_368  # at least the algorithmic bytes
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
