@@ -28,6 +28,7 @@ EXPORTS = (
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
     "bca_staircase_groups_fwd", "bca_staircase_groups_bwd", "bca_decode_fp8",
+    "bca_staircase_bwd_stage",
 )
 
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.bca_staircase_bwd.restype = _I
     L.bca_staircase_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                     _I, _I, _I, _F, _I, _P, _S, _P]
+    L.bca_staircase_bwd_stage.restype = _I
+    L.bca_staircase_bwd_stage.argtypes = [_I] + L.bca_staircase_bwd.argtypes
     L.bca_decode_workspace.restype = _S
     L.bca_decode_workspace.argtypes = [_I, _I, _I, _I, _I, _I]
     L.bca_decode.restype = _I
@@ -146,9 +149,34 @@ def _need_gpu(*ts: Optional[torch.Tensor]) -> torch.device:
     return dev
 
 
+def _expect(func: str, t: Optional[torch.Tensor], name: str, shape, dtype) -> None:
+    """Raise BcaError unless tensor t (if given) has this shape and dtype."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise BcaError(func, 2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise BcaError(func, 3, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _packed_shapes(func: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   dtypes=(torch.bfloat16, torch.float32)):
+    """(total, hq, hkv, d) of packed inputs, after checking that q is
+    [total, hq, d] and k, v are [total, hkv, d] of q's dtype."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise BcaError(func, 2, "q must be [total, hq, d] and k, v [total, hkv, d]")
+    if q.dtype not in dtypes:
+        raise BcaError(func, 3, f"q must be one of {dtypes}, got {q.dtype}")
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    _expect(func, k, "k", (total, hkv, d), q.dtype)
+    _expect(func, v, "v", (total, hkv, d), q.dtype)
+    return total, hq, hkv, d
+
+
 def _seq_args(cu_seqlens: torch.Tensor, max_seqlen: Optional[int]):
-    if cu_seqlens.dtype != torch.int32:
-        raise BcaError("args", 2, "cu_seqlens must be int32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise BcaError("args", 2, "cu_seqlens must be a 1-D int32 tensor of nseq + 1 entries")
     nseq = cu_seqlens.numel() - 1
     if max_seqlen is None:  # convenience: one device-to-host read
         max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
@@ -166,14 +194,12 @@ def staircase_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens:
     [nseq + 1] and s_copies int32 [nseq] on the same GPU.  LSE is [hq, total]
     float32 (natural log).
     """
-    dev = _need_gpu(q, k, v, cu_seqlens, s_copies, out, lse)
-    total, hq, d = q.shape
-    hkv = k.shape[1]
-    if k.shape != (total, hkv, d) or v.shape != k.shape:
-        raise BcaError("staircase_fwd", 2, "k and v must be [total, hkv, d] matching q")
+    total, hq, hkv, d = _packed_shapes("staircase_fwd", q, k, v)
+    _expect("staircase_fwd", out, "out", (total, hq, d), q.dtype)
+    _expect("staircase_fwd", lse, "lse", (hq, total), torch.float32)
     nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
-    if s_copies is not None and (s_copies.dtype != torch.int32 or s_copies.numel() != nseq):
-        raise BcaError("staircase_fwd", 2, "s_copies must be int32 [nseq]")
+    _expect("staircase_fwd", s_copies, "s_copies", (nseq,), torch.int32)
+    dev = _need_gpu(q, k, v, cu_seqlens, s_copies, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -191,12 +217,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
         out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Block-causal forward over packed sequences -> (O, LSE); see staircase_fwd."""
-    dev = _need_gpu(q, k, v, cu_seqlens, out, lse)
-    total, hq, d = q.shape
-    hkv = k.shape[1]
-    if k.shape != (total, hkv, d) or v.shape != k.shape:
-        raise BcaError("fwd", 2, "k and v must be [total, hkv, d] matching q")
+    total, hq, hkv, d = _packed_shapes("fwd", q, k, v)
+    _expect("fwd", out, "out", (total, hq, d), q.dtype)
+    _expect("fwd", lse, "lse", (hq, total), torch.float32)
     nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
+    dev = _need_gpu(q, k, v, cu_seqlens, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -214,7 +239,8 @@ def _groups_args(func, group_start, group_pe, group_copies, nseq):
                     (group_copies, "group_copies")):
         if t is None or t.dtype != torch.int32:
             raise BcaError(func, 2, f"{name} must be an int32 tensor")
-    if group_start.numel() != nseq + 1 or group_pe.numel() != group_copies.numel():
+    if (group_start.dim() != 1 or group_pe.dim() != 1 or group_copies.dim() != 1
+            or group_start.numel() != nseq + 1 or group_pe.numel() != group_copies.numel()):
         raise BcaError(func, 2, "group_start must be [nseq + 1]; group_pe and group_copies "
                                 "must have one entry per group")
 
@@ -227,13 +253,12 @@ def staircase_groups_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """General trajectory staircase forward -> (O, LSE): copy groups per segment,
     group g's copies seeing the clean keys [0, group_pe[g])."""
-    dev = _need_gpu(q, k, v, cu_seqlens, group_start, group_pe, group_copies, out, lse)
-    total, hq, d = q.shape
-    hkv = k.shape[1]
-    if k.shape != (total, hkv, d) or v.shape != k.shape:
-        raise BcaError("staircase_groups_fwd", 2, "k and v must be [total, hkv, d] matching q")
+    total, hq, hkv, d = _packed_shapes("staircase_groups_fwd", q, k, v)
+    _expect("staircase_groups_fwd", out, "out", (total, hq, d), q.dtype)
+    _expect("staircase_groups_fwd", lse, "lse", (hq, total), torch.float32)
     nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
     _groups_args("staircase_groups_fwd", group_start, group_pe, group_copies, nseq)
+    dev = _need_gpu(q, k, v, cu_seqlens, group_start, group_pe, group_copies, out, lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -247,6 +272,20 @@ def staircase_groups_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+def _bwd_checks(func: str, q, k, v, o, lse, dout, dq, dk, dv, workspace):
+    """Shapes and dtypes of a backward call: everything bf16, o/dout/dq like q,
+    dk/dv like k, lse float32 [hq, total], the workspace a 1-D byte buffer."""
+    total, hq, hkv, d = _packed_shapes(func, q, k, v, dtypes=(torch.bfloat16,))
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(func, t, name, (total, hq, d), torch.bfloat16)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _expect(func, t, name, (total, hkv, d), torch.bfloat16)
+    _expect(func, lse, "lse", (hq, total), torch.float32)
+    if workspace is not None and workspace.dim() != 1:
+        raise BcaError(func, 2, "workspace must be a 1-D buffer")
+    return total, hq, hkv, d
+
+
 def staircase_groups_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                          lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor,
                          group_start: torch.Tensor, group_pe: torch.Tensor,
@@ -256,10 +295,10 @@ def staircase_groups_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
                          dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                          dv: Optional[torch.Tensor] = None):
     """General trajectory staircase backward -> (dQ, dK, dV), bf16."""
+    total, hq, hkv, d = _bwd_checks("staircase_groups_bwd", q, k, v, o, lse, dout, dq, dk, dv,
+                                    workspace)
     dev = _need_gpu(q, k, v, o, lse, dout, cu_seqlens, group_start, group_pe, group_copies,
                     workspace, dq, dk, dv)
-    total, hq, d = q.shape
-    hkv = k.shape[1]
     nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
     _groups_args("staircase_groups_bwd", group_start, group_pe, group_copies, nseq)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -290,11 +329,16 @@ def staircase_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
                   scale: Optional[float] = None, max_seqlen: Optional[int] = None,
                   workspace: Optional[torch.Tensor] = None,
                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                  dv: Optional[torch.Tensor] = None):
-    """Backward -> (dQ, dK, dV), bf16.  o and lse come from staircase_fwd."""
+                  dv: Optional[torch.Tensor] = None, stage: int = 0):
+    """Backward -> (dQ, dK, dV), bf16.  o and lse come from staircase_fwd.
+
+    ``stage`` selects bca_staircase_bwd_stage: 0 runs everything; 1 the row
+    terms, 2 dK/dV and 3 dQ (2 and 3 need the workspace stage 1 filled)."""
+    total, hq, hkv, d = _bwd_checks("staircase_bwd", q, k, v, o, lse, dout, dq, dk, dv,
+                                    workspace)
+    nseq = cu_seqlens.numel() - 1
+    _expect("staircase_bwd", s_copies, "s_copies", (nseq,), torch.int32)
     dev = _need_gpu(q, k, v, o, lse, dout, cu_seqlens, s_copies, workspace, dq, dk, dv)
-    total, hq, d = q.shape
-    hkv = k.shape[1]
     nseq, max_seqlen = _seq_args(cu_seqlens, max_seqlen)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = staircase_bwd_workspace(total, hq, hkv, d)
@@ -303,12 +347,13 @@ def staircase_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib().bca_staircase_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), _ptr(s_copies),
-                                 nseq, max_seqlen, total, hq, hkv, d, int(block_size), scale,
-                                 _dtype_code(q), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(dev))
-    _check("bca_staircase_bwd", st)
+    st = lib().bca_staircase_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(cu_seqlens), _ptr(s_copies), nseq, max_seqlen, total,
+                                       hq, hkv, d, int(block_size), scale, _dtype_code(q),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("bca_staircase_bwd_stage", st)
     return dq, dk, dv
 
 
@@ -317,14 +362,37 @@ def decode_workspace(q_len: int, kv_len: int, hq: int, hkv: int, d: int,
     return int(lib().bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits))
 
 
+def _decode_shapes(func: str, q, k, v, out, lse, kv_dtype):
+    """(q_len, hq, kv_len, hkv, d) of a decode call after checking q [q_len,
+    hq, d] bf16, k/v [kv_len, hkv, d] of kv_dtype (None: any one-byte type),
+    out like q and lse float32 [hq, q_len]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise BcaError(func, 2, "q must be [q_len, hq, d] and k, v [kv_len, hkv, d]")
+    if q.dtype != torch.bfloat16:
+        raise BcaError(func, 3, f"q must be torch.bfloat16, got {q.dtype}")
+    q_len, hq, d = q.shape
+    kv_len, hkv = k.shape[0], k.shape[1]
+    if kv_dtype is None:
+        for t, name in ((k, "k8"), (v, "v8")):
+            if t.element_size() != 1:
+                raise BcaError(func, 3, f"{name} must hold one byte per element")
+        _expect(func, k, "k8", (kv_len, hkv, d), None)
+        _expect(func, v, "v8", (kv_len, hkv, d), None)
+    else:
+        _expect(func, k, "k", (kv_len, hkv, d), kv_dtype)
+        _expect(func, v, "v", (kv_len, hkv, d), kv_dtype)
+    _expect(func, out, "out", (q_len, hq, d), torch.bfloat16)
+    _expect(func, lse, "lse", (hq, q_len), torch.float32)
+    return q_len, hq, kv_len, hkv, d
+
+
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
            num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode step -> (O [q_len, hq, d], LSE [hq, q_len]); k/v hold prefix + block rows."""
+    q_len, hq, kv_len, hkv, d = _decode_shapes("decode", q, k, v, out, lse, torch.bfloat16)
     dev = _need_gpu(q, k, v, workspace, out, lse)
-    q_len, hq, d = q.shape
-    kv_len, hkv = k.shape[0], k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
     if workspace is None and need > 0:
@@ -350,15 +418,8 @@ def decode_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: flo
     k8/v8 are [kv_len, hkv, d] uint8 (or float8_e4m3fn) holding K / k_scale
     and V / v_scale.
     """
+    q_len, hq, kv_len, hkv, d = _decode_shapes("decode_fp8", q, k8, v8, out, lse, None)
     dev = _need_gpu(q, k8, v8, workspace, out, lse)
-    if k8.element_size() != 1 or v8.element_size() != 1:
-        raise BcaError("decode_fp8", 3, "k8 and v8 must hold one byte per element")
-    if q.dtype != torch.bfloat16:
-        raise BcaError("decode_fp8", 3, "q must be bfloat16")
-    q_len, hq, d = q.shape
-    kv_len, hkv = k8.shape[0], k8.shape[1]
-    if k8.shape != (kv_len, hkv, d) or v8.shape != k8.shape:
-        raise BcaError("decode_fp8", 2, "k8 and v8 must be [kv_len, hkv, d]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
     if workspace is None and need > 0:
@@ -387,9 +448,9 @@ class DecodeGraph:
                  scale: Optional[float] = None, num_splits: int = 0,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None):
+        q_len, hq, kv_len, hkv, d = _decode_shapes("DecodeGraph", q, k, v, out, lse,
+                                                   torch.bfloat16)
         dev = _need_gpu(q, k, v, workspace, out, lse)
-        q_len, hq, d = q.shape
-        kv_len, hkv = k.shape[0], k.shape[1]
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
         need = decode_workspace(q_len, kv_len, hq, hkv, d, num_splits)
         if workspace is None and need > 0:

@@ -845,10 +845,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a, int hpw, int 
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, int stage, hipStream_t stream) {
   if (a.nseq <= 0 || a.total <= 0) return hipSuccess;
   // 1. delta
-  {
+  if (stage == 0 || stage == 1) {
     const long long nrows = (long long)a.total * a.hq;
     const int rows_per_wg = 256 / (a.d / 8);
     const long long nwg = (nrows + rows_per_wg - 1) / rows_per_wg;
@@ -857,7 +857,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     if (err != hipSuccess) return err;
   }
   // 2. dK, dV
-  {
+  if (stage == 0 || stage == 2) {
     const long long nkt = (max_seqlen + kKvKeys - 1) / kKvKeys;
     const long long nwg = nkt * a.nseq * a.hkv;
     if (a.d == 128) {
@@ -871,7 +871,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     if (err != hipSuccess) return err;
   }
   // 3. dQ
-  {
+  if (stage == 0 || stage == 3) {
     const int hpw = heads_per_wg(a.hq, a.hkv);
     const int tok = 32 * (8 / hpw);
     const long long ntiles = (max_seqlen + tok - 1) / tok;
@@ -885,6 +885,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream)
     }
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
 }  // namespace bca

@@ -2,13 +2,20 @@
 //
 // Every check that needs only host-visible values runs before anything is
 // enqueued, so an invalid call returns a status and leaves the stream alone.
-// Nothing here allocates, frees or synchronises.
+// Nothing here allocates device memory, frees or synchronises -- except that
+// with BCA_VALIDATE=1 in the environment the packed entry points copy their
+// device tables (cu_seqlens, s_copies, the copy-group table) to the host,
+// synchronising the stream, and check them before any launch.  With
+// BCA_POISON=1 every workspace is filled with NaN words before the kernels
+// that use it run, so that a read of a workspace word no kernel wrote shows.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/bca.h"
 #include "bca_kernels.hpp"
@@ -31,8 +38,16 @@ bca_status_t hip_status(hipError_t err, const char* what) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kPoisonWord = 0x7FC00000u;  // quiet NaN
+
+// An environment switch is on when set to anything but "" or "0".  Read at
+// every call, so a process may turn it on and off between calls.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
 constexpr int kMaxDecodeSplits = 256;
-constexpr int kMaxGraphSteps = 4096;  // decode steps one captured graph may hold  // the combine kernel stages one weight per split and row
+constexpr int kMaxGraphSteps = 4096;  // decode steps one captured graph may hold
 
 // Checks shared by the packed-segment entry points.
 bca_status_t check_packed(const void* q, const void* k, const void* v, const void* o,
@@ -44,7 +59,8 @@ bca_status_t check_packed(const void* q, const void* k, const void* v, const voi
   if (hq % hkv != 0) return fail(BCA_ERR_SHAPE, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
   if (d != 64 && d != 128) return fail(BCA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
   if (block_size < 1) return fail(BCA_ERR_SHAPE, "block_size must be >= 1 (got %d)", block_size);
-  if (!std::isfinite(scale)) return fail(BCA_ERR_SHAPE, "scale must be finite");
+  if (!std::isfinite(scale) || scale <= 0.f)
+    return fail(BCA_ERR_SHAPE, "scale must be finite and > 0");
   if (nseq == 0 || total == 0) return BCA_OK;
   if (max_seqlen < 1) return fail(BCA_ERR_SHAPE, "max_seqlen must be >= 1 when total > 0");
   if (!q || !k || !v || !o || !lse || !cu) return fail(BCA_ERR_NULL, "a required pointer is NULL");
@@ -54,13 +70,97 @@ bca_status_t check_packed(const void* q, const void* k, const void* v, const voi
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+template <typename T>
+hipError_t to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.assign(n, T{});
+  if (n == 0) return hipSuccess;
+  return hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
+}
+
+// BCA_VALIDATE: the device tables of a packed call, checked on the host
+// before anything is enqueued (this copies them and synchronises `s`).
+//   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[nseq] = total, every
+//   length <= max_seqlen; per segment S >= 0 copies, P = L - S B >= 0 and,
+//   with copies, P % B = 0; copy groups: group_start non-decreasing from 0,
+//   each pe a multiple of B in [0, P], non-decreasing within the segment,
+//   copies >= 0.
+bca_status_t validate_tables(const int32_t* cu, const int32_t* s_copies, const int32_t* gstart,
+                             const int32_t* gpe, const int32_t* gcp, int32_t nseq,
+                             int32_t max_seqlen, int32_t total, int32_t B, hipStream_t s) {
+  std::vector<int32_t> hcu, hsc, hgs, hpe, hcp;
+  hipError_t err = to_host(hcu, cu, (size_t)nseq + 1, s);
+  if (err == hipSuccess && s_copies) err = to_host(hsc, s_copies, (size_t)nseq, s);
+  if (err == hipSuccess && gstart) err = to_host(hgs, gstart, (size_t)nseq + 1, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_status(err, "validation copy");
+  if (hcu[0] != 0) return fail(BCA_ERR_SHAPE, "validation: cu_seqlens[0] = %d, not 0", hcu[0]);
+  for (int32_t i = 0; i < nseq; ++i) {
+    const long long L = (long long)hcu[i + 1] - hcu[i];
+    if (L < 0) return fail(BCA_ERR_SHAPE, "validation: cu_seqlens decreases at segment %d", i);
+    if (L > max_seqlen)
+      return fail(BCA_ERR_SHAPE, "validation: segment %d has %lld tokens > max_seqlen %d", i, L,
+                  max_seqlen);
+  }
+  if (hcu[nseq] != total)
+    return fail(BCA_ERR_SHAPE, "validation: cu_seqlens[nseq] = %d, total = %d", hcu[nseq], total);
+  if (gstart) {
+    if (hgs[0] != 0) return fail(BCA_ERR_SHAPE, "validation: group_start[0] = %d, not 0", hgs[0]);
+    for (int32_t i = 0; i < nseq; ++i)
+      if (hgs[i + 1] < hgs[i])
+        return fail(BCA_ERR_SHAPE, "validation: group_start decreases at segment %d", i);
+    if (hgs[nseq] > (1 << 26))
+      return fail(BCA_ERR_SHAPE, "validation: group_start[nseq] = %d groups", hgs[nseq]);
+    err = to_host(hpe, gpe, (size_t)hgs[nseq], s);
+    if (err == hipSuccess) err = to_host(hcp, gcp, (size_t)hgs[nseq], s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return hip_status(err, "validation copy");
+  }
+  for (int32_t i = 0; i < nseq; ++i) {
+    const long long L = (long long)hcu[i + 1] - hcu[i];
+    long long S = 0;
+    if (gstart) {
+      for (int32_t g = hgs[i]; g < hgs[i + 1]; ++g) {
+        if (hcp[g] < 0) return fail(BCA_ERR_SHAPE, "validation: group %d has %d copies", g, hcp[g]);
+        S += hcp[g];
+      }
+    } else if (s_copies) {
+      S = hsc[i];
+      if (S < 0) return fail(BCA_ERR_SHAPE, "validation: segment %d has %lld copies", i, S);
+    }
+    const long long P = L - S * B;
+    if (P < 0)
+      return fail(BCA_ERR_SHAPE, "validation: segment %d: %lld copies of %d exceed %lld tokens",
+                  i, S, B, L);
+    if (S > 0 && P % B != 0)
+      return fail(BCA_ERR_SHAPE, "validation: segment %d: prefix %lld is not a multiple of %d",
+                  i, P, B);
+    if (gstart) {
+      long long prev = 0;
+      for (int32_t g = hgs[i]; g < hgs[i + 1]; ++g) {
+        const long long pe = hpe[g];
+        if (pe % B != 0 || pe < 0 || pe > P || pe < prev)
+          return fail(BCA_ERR_SHAPE,
+                      "validation: group %d: prefix end %lld must be a multiple of B in [%lld, "
+                      "%lld]",
+                      g, pe, prev, P);
+        prev = pe;
+      }
+    }
+  }
+  return BCA_OK;
+}
+
+bca_status_t poison(void* p, size_t bytes, hipStream_t s) {
+  return hip_status(bca::launch_fill_u32(p, bytes / 4, kPoisonWord, s), "poison fill");
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t bca_abi_version(void) { return BCA_ABI_VERSION; }
 
-const char* bca_status_string(int32_t status) {
+const char* bca_status_string(bca_status_t status) {
   switch (status) {
     case BCA_OK: return "ok";
     case BCA_ERR_NULL: return "null pointer";
@@ -93,6 +193,11 @@ static bca_status_t fwd_impl(const void* q, const void* k, const void* v, void* 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BCA_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (env_on("BCA_VALIDATE")) {
+    st = validate_tables(cu_seqlens, s_copies, group_start, group_pe, group_copies, nseq,
+                         max_seqlen, total, block_size, s);
+    if (st != BCA_OK) return st;
+  }
   if (dtype == BCA_BF16) {
     bca::FwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -185,7 +290,8 @@ static bca_status_t bwd_impl(const void* q, const void* k, const void* v, const 
                              const int32_t* group_copies, int32_t nseq, int32_t max_seqlen,
                              int32_t total, int32_t hq, int32_t hkv, int32_t d,
                              int32_t block_size, float scale, bca_dtype_t dtype, void* workspace,
-                             size_t ws_bytes, void* stream) {
+                             size_t ws_bytes, int32_t stage, void* stream) {
+  if (stage < 0 || stage > 3) return fail(BCA_ERR_SHAPE, "stage must be 0, 1, 2 or 3 (got %d)", stage);
   bca_status_t st = check_packed(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total, hq, hkv,
                                  d, block_size, scale);
   if (st != BCA_OK) return st;
@@ -224,8 +330,18 @@ static bca_status_t bwd_impl(const void* q, const void* k, const void* v, const 
   a.block_size = block_size;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  return hip_status(bca::launch_bwd_bf16(a, max_seqlen, static_cast<hipStream_t>(stream)),
-                    "backward launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (env_on("BCA_VALIDATE")) {
+    st = validate_tables(cu_seqlens, s_copies, group_start, group_pe, group_copies, nseq,
+                         max_seqlen, total, block_size, s);
+    if (st != BCA_OK) return st;
+  }
+  // The row terms are written by stage 1; later stages only read them.
+  if ((stage == 0 || stage == 1) && env_on("BCA_POISON")) {
+    st = poison(workspace, need, s);
+    if (st != BCA_OK) return st;
+  }
+  return hip_status(bca::launch_bwd_bf16(a, max_seqlen, stage, s), "backward launch");
 }
 
 extern "C" {
@@ -239,7 +355,20 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
   g_last_error[0] = '\0';
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, s_copies, nullptr, nullptr,
                   nullptr, nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype,
-                  workspace, ws_bytes, stream);
+                  workspace, ws_bytes, 0, stream);
+}
+
+bca_status_t bca_staircase_bwd_stage(int32_t stage, const void* q, const void* k, const void* v,
+                                     const void* o, const float* lse, const void* dout, void* dq,
+                                     void* dk, void* dv, const int32_t* cu_seqlens,
+                                     const int32_t* s_copies, int32_t nseq, int32_t max_seqlen,
+                                     int32_t total, int32_t hq, int32_t hkv, int32_t d,
+                                     int32_t block_size, float scale, bca_dtype_t dtype,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, s_copies, nullptr, nullptr,
+                  nullptr, nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype,
+                  workspace, ws_bytes, stage, stream);
 }
 
 bca_status_t bca_staircase_groups_bwd(const void* q, const void* k, const void* v,
@@ -256,7 +385,7 @@ bca_status_t bca_staircase_groups_bwd(const void* q, const void* k, const void* 
     return fail(BCA_ERR_NULL, "group_start, group_pe and group_copies are required");
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, nullptr, group_start, group_pe,
                   group_copies, nseq, max_seqlen, total, hq, hkv, d, block_size, scale, dtype,
-                  workspace, ws_bytes, stream);
+                  workspace, ws_bytes, 0, stream);
 }
 
 // Split-KV plan of the decode step: the 64-key tiles are dealt evenly to
@@ -309,7 +438,8 @@ static bca_status_t decode_args(const void* q, const void* k, const void* v, voi
   if (hq <= 0 || hkv <= 0 || hq % hkv)
     return fail(BCA_ERR_SHAPE, "hq (%d) must be a positive multiple of hkv (%d)", hq, hkv);
   if (d != 64 && d != 128) return fail(BCA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
-  if (!std::isfinite(scale)) return fail(BCA_ERR_SHAPE, "scale must be finite");
+  if (!std::isfinite(scale) || scale <= 0.f)
+    return fail(BCA_ERR_SHAPE, "scale must be finite and > 0");
   if (num_splits < 0 || num_splits > kMaxDecodeSplits)
     return fail(BCA_ERR_SHAPE, "num_splits must be in [0, %d]", kMaxDecodeSplits);
   if (dtype != BCA_BF16) return fail(BCA_ERR_DTYPE, "decode supports bf16 only");
@@ -344,6 +474,18 @@ static bca_status_t decode_args(const void* q, const void* k, const void* v, voi
   return BCA_OK;
 }
 
+// Enqueue a decode step: with BCA_POISON the partial buffers are NaN-filled
+// first (only the kernels' own writes may reach the combine).
+static hipError_t decode_enqueue(const bca::DecodeArgs& a, bool fp8, hipStream_t s) {
+  if (a.nsplit > 1 && env_on("BCA_POISON")) {
+    const size_t rows = (size_t)a.nsplit * a.hq * ((a.q_len + 31) / 32) * 32;
+    hipError_t err = bca::launch_fill_u32(a.part_o, rows * a.d, kPoisonWord, s);
+    if (err == hipSuccess) err = bca::launch_fill_u32(a.part_lse, rows, kPoisonWord, s);
+    if (err != hipSuccess) return err;
+  }
+  return fp8 ? bca::launch_decode_fp8(a, s) : bca::launch_decode_bf16(a, s);
+}
+
 struct bca_decode_graph {
   hipGraph_t graph;
   hipGraphExec_t exec;
@@ -361,7 +503,7 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
                                       num_splits, workspace, ws_bytes, &a);
   if (st != BCA_OK) return st;
-  return hip_status(bca::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "decode launch");
+  return hip_status(decode_enqueue(a, false, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
 bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float k_scale,
@@ -381,7 +523,7 @@ bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float
   a.v = nullptr;
   a.scale_log2 *= k_scale;
   a.o_mul = v_scale;
-  return hip_status(bca::launch_decode_fp8(a, static_cast<hipStream_t>(stream)), "decode launch");
+  return hip_status(decode_enqueue(a, true, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
 bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,
@@ -408,7 +550,7 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
   }
   hipError_t launch_err = hipSuccess;
   for (int32_t i = 0; i < steps && launch_err == hipSuccess; ++i)
-    launch_err = bca::launch_decode_bf16(a, s);
+    launch_err = decode_enqueue(a, false, s);
   hipGraph_t g = nullptr;
   err = hipStreamEndCapture(s, &g);
   (void)hipStreamDestroy(s);

@@ -93,6 +93,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int max_seqlen, hipStream_t stream)
 hipError_t launch_fwd_f32(const FwdF32Args& a, int max_seqlen, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, hipStream_t stream);
+// Backward kernels: stage 0 = all three in order, 1 = row terms (delta and
+// LSE * log2 e), 2 = dK/dV, 3 = dQ.
+hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, int stage, hipStream_t stream);
+
+// p[0 .. nwords) = value (a grid-stride fill kernel).
+hipError_t launch_fill_u32(void* p, size_t nwords, uint32_t value, hipStream_t stream);
 
 }  // namespace bca

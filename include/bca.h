@@ -40,14 +40,33 @@
  * included.  The library never allocates, frees or synchronises: each call
  * only enqueues kernels on `stream` and returns.  Inputs are read-only and
  * outputs must not alias inputs.  Device-array contents (cu_seqlens,
- * s_copies) are the caller's contract and are not checked.
+ * s_copies, the copy-group tables) and max_seqlen >= every segment length
+ * are the caller's contract: they are not read on the host unless
+ * BCA_VALIDATE is set (below).  A max_seqlen below a segment's length leaves
+ * that segment's first query tiles unwritten.
  *
  * Errors: every host-detectable fault (NULL pointer, bad shape or size,
- * unsupported head_dim or dtype, workspace too small) is reported by the
- * return value before anything is enqueued.  A failed kernel launch returns
- * BCA_ERR_HIP.  bca_last_error() gives a message for the calling thread's most
- * recent failure.  Faults inside kernels surface at the caller's next
- * synchronisation, as with any asynchronous GPU work.
+ * unsupported head_dim or dtype, scale not finite or not > 0, workspace too
+ * small) is reported by the return value before anything is enqueued.  A
+ * failed kernel launch returns BCA_ERR_HIP.  bca_last_error() gives a message
+ * for the calling thread's most recent failure.  Faults inside kernels
+ * surface at the caller's next synchronisation, as with any asynchronous GPU
+ * work.
+ *
+ * Environment switches (read at every call; on = set and not "0"):
+ *   BCA_VALIDATE  the packed entry points copy cu_seqlens, s_copies and the
+ *                 copy-group tables to the host (synchronising `stream`) and
+ *                 check them before any launch: cu_seqlens[0] = 0,
+ *                 non-decreasing, cu_seqlens[nseq] = total, every length
+ *                 <= max_seqlen; per segment S >= 0, P = L - S*B >= 0 and,
+ *                 with copies, P % B == 0; group_start[0] = 0 and
+ *                 non-decreasing, every pe a multiple of B in [0, P] and
+ *                 non-decreasing within its segment, copies >= 0.  A table
+ *                 that fails returns BCA_ERR_SHAPE and nothing is enqueued.
+ *                 Not for use under graph capture (it synchronises).
+ *   BCA_POISON    workspaces are filled with NaN words (by a fill kernel on
+ *                 `stream`) before the kernels that use them, so that reading
+ *                 a word no kernel wrote shows up in the outputs.
  */
 #ifndef BCA_H
 #define BCA_H
@@ -76,8 +95,9 @@ typedef enum { BCA_F32 = 0, BCA_BF16 = 1 } bca_dtype_t;
 /* Version of this ABI (BCA_ABI_VERSION of the built library). */
 int32_t bca_abi_version(void);
 
-/* Static, human-readable name of a status code. */
-const char* bca_status_string(int32_t status);
+/* Static, human-readable name of a status code ("unknown status" for values
+ * outside the enumeration). */
+const char* bca_status_string(bca_status_t status);
 
 /* Message describing the calling thread's most recent failure ("" if none).
  * The string is owned by the library and valid until the next call from the
@@ -95,7 +115,8 @@ const char* bca_last_error(void);
  *   total       : number of packed tokens (cu_seqlens[nseq])
  *   hq, hkv, d  : query heads, KV heads, head_dim; d in {64, 128}
  *   block_size  : B >= 1
- *   scale       : multiplies q.k before the softmax (typically 1/sqrt(d))
+ *   scale       : multiplies q.k before the softmax (typically 1/sqrt(d));
+ *                 finite and > 0
  * Every row of o and lse for the `total` tokens is written.
  * Equivalent to bca_staircase_fwd with s_copies = NULL.
  */
@@ -140,6 +161,27 @@ bca_status_t bca_staircase_bwd(const void* q, const void* k, const void* v, cons
                                int32_t hkv, int32_t d, int32_t block_size, float scale,
                                bca_dtype_t dtype, void* workspace, size_t ws_bytes,
                                void* stream);
+
+/*
+ * One stage of bca_staircase_bwd, same arguments (the same formulas:
+ * dS = P * (dP - delta) with delta = rowsum(dO * O), dK = scale dS^T Q,
+ * dV = P^T dO, dQ = scale dS K):
+ *   stage 1 : the row terms -- delta and LSE * log2(e) -- into the workspace
+ *   stage 2 : dK and dV (reads the row terms)
+ *   stage 3 : dQ (reads the row terms)
+ *   stage 0 : all three in order (= bca_staircase_bwd)
+ * Stages 2 and 3 need stage 1's workspace contents and are independent of
+ * each other: after stage 1 has completed they may run in either order, or
+ * concurrently on two streams.  This lets a caller time the kernels one by
+ * one or overlap them with other work.  stage outside 0..3: BCA_ERR_SHAPE.
+ */
+bca_status_t bca_staircase_bwd_stage(int32_t stage, const void* q, const void* k, const void* v,
+                                     const void* o, const float* lse, const void* dout, void* dq,
+                                     void* dk, void* dv, const int32_t* cu_seqlens,
+                                     const int32_t* s_copies, int32_t nseq, int32_t max_seqlen,
+                                     int32_t total, int32_t hq, int32_t hkv, int32_t d,
+                                     int32_t block_size, float scale, bca_dtype_t dtype,
+                                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * General trajectory staircase (paper cards page, Figure 3 caption; thread

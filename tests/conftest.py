@@ -10,6 +10,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: a full-size parity case whose fp64 oracle takes "
+                                       "tens of seconds on the host")
 
 
 @pytest.fixture(autouse=True)

@@ -153,3 +153,38 @@ def test_decode_graph_checks(L):
     assert create(handle=None) == NULL
     L.bca_decode_graph_destroy(None)  # no-op
     assert L.bca_decode_graph_launch(None, None) == NULL
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf")])
+def test_scale_must_be_positive_and_finite(L, scale):
+    # The kernels take the row maximum of the raw scores before scaling, which
+    # is the maximum of the scaled scores only for a positive scale.
+    assert fwd(L, scale=scale) == SHAPE
+    assert L.bca_staircase_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               1, 64, 64, 32, 8, 128, 32, scale, BF16, FAKE, 1 << 30,
+                               None) == SHAPE
+    assert L.bca_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 32, 1056, 32, 8, 128, scale, BF16, 0, FAKE,
+                        1 << 30, None) == SHAPE
+    assert b"scale" in L.bca_last_error()
+
+
+def stage_call(L, stage, **kw):
+    a = dict(ws=FAKE, nseq=1)
+    a.update(kw)
+    return L.bca_staircase_bwd_stage(stage, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None, a["nseq"], 1000, 1000, 32, 8, 128, 32, 0.1, BF16,
+                                     a["ws"], 1 << 30, None)
+
+
+def test_backward_stage_checks(L):
+    for bad in (-1, 4, 99):
+        assert stage_call(L, bad) == SHAPE
+        assert b"stage" in L.bca_last_error()
+    for stage in (0, 1, 2, 3):  # valid stages still check the workspace, before any launch
+        assert stage_call(L, stage, ws=None) == WS
+        assert stage_call(L, stage, nseq=0) == OK
+
+
+def test_status_strings_cover_every_code(L):
+    names = {L.bca_status_string(c) for c in range(7)}
+    assert len(names) == 7 and b"unknown status" not in names

@@ -1,11 +1,14 @@
 """GPU parity of the backward (dQ, dK, dV) with the oracle.
 
-Small problems: every element.  The 16-trajectory workload: dQ on sampled rows
-(each row's gradient is computed alone by the oracle), dK and dV of whole
-segments for the two shortest trajectories, and for every segment the two
-invariants that hold at any size: dK sums to zero over a segment and dV sums
-to the group's summed dO.
-Tolerance: max|err| <= 1e-2 * max|ref| per gradient tensor.
+Small problems: every element.  The 16-trajectory workload: O, LSE, dQ, dK
+and dV of the longest trajectory (9,472 tokens) element by element, one test
+per KV head with its four query heads (marked slow: 4.4 TFLOP of dense fp64
+oracle work in all); dQ, dK and dV of the two shortest trajectories whole;
+dQ on sampled rows of every trajectory (each row's gradient is computed alone
+by the oracle); and for every segment the two invariants that hold at any
+size: dK sums to zero over a segment and dV sums to the group's summed dO.
+Tolerance: max|err| <= 1e-2 * max|ref| per gradient tensor (per compared
+slice, which is never looser than per whole tensor).
 """
 import numpy as np
 import pytest
@@ -43,6 +46,7 @@ SMALL = [
     ("staircase_B8_d64", [40 + 3 * 8, 8 * 9 + 7 * 8], [3, 7], 4, 2, 64, 8),
     ("staircase_no_prefix", [4 * 32], [4], 8, 8, 128, 32),
     ("with_empty_segment", [64, 0, 100], [0, 0, 0], 4, 2, 128, 16),
+    ("mixed_S0_and_S", [96, 64 + 3 * 32, 128, 32 + 2 * 32, 45], [0, 3, 0, 2, 0], 8, 2, 128, 32),
 ]
 
 
@@ -86,6 +90,43 @@ def test_16traj_whole_segments(big):
         errs = [rel_err(dq[a:b], dQ), rel_err(dk[a:b], dK), rel_err(dv[a:b], dV)]
         print(f"segment {s} (L={b - a}): rel err dQ {errs[0]:.3g} dK {errs[1]:.3g} dV {errs[2]:.3g}")
         assert max(errs) <= TOL_GRAD, errs
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("g", range(8))
+def test_16traj_longest_trajectory_whole(big, g):
+    """Forward and backward of the longest trajectory for KV head g and its
+    query heads, against the oracle run on exactly that slice (the other
+    heads of the segment do not touch these outputs)."""
+    w, (dq, dk, dv) = big
+    s = int(np.argmax(np.diff(w.cu_seqlens)))
+    a, b = int(w.cu_seqlens[s]), int(w.cu_seqlens[s + 1])
+    grp = w.hq // w.hkv
+    hs = slice(g * grp, (g + 1) * grp)
+    O, LSE, dQ, dK, dV = oracle.attention_bwd(w.q[a:b, hs], w.k[a:b, g:g + 1], w.v[a:b, g:g + 1],
+                                              w.do[a:b, hs], [0, b - a], [int(w.s_copies[s])],
+                                              w.block_size, w.scale)
+    o, lse = big_forward(w)
+    eo, el = max_abs(o[a:b, hs], O), max_abs(lse[hs, a:b], LSE)
+    errs = [rel_err(dq[a:b, hs], dQ), rel_err(dk[a:b, g:g + 1], dK), rel_err(dv[a:b, g:g + 1], dV)]
+    print(f"segment {s} (L={b - a}) KV head {g}: max|dO| {eo:.3g} max|dLSE| {el:.3g}; rel err "
+          f"dQ {errs[0]:.3g} dK {errs[1]:.3g} dV {errs[2]:.3g}")
+    assert eo <= 1e-2 and el <= 1e-2, (eo, el)
+    assert max(errs) <= TOL_GRAD, errs
+
+
+_FWD = {}
+
+
+def big_forward(w):
+    """O and LSE of the 16-trajectory forward as float64 (computed once)."""
+    if "o" not in _FWD:
+        q, k, v, cu, sc, _ = device_inputs(w)
+        o, lse = bca.staircase_fwd(q, k, v, cu, sc, w.block_size, w.scale, w.max_seqlen)
+        torch.cuda.synchronize()
+        _FWD["o"] = o.float().cpu().numpy().astype(np.float64)
+        _FWD["lse"] = lse.cpu().numpy().astype(np.float64)
+    return _FWD["o"], _FWD["lse"]
 
 
 def test_16traj_invariants_every_segment(big):

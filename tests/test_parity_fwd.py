@@ -1,8 +1,11 @@
 """GPU parity of the forward kernels (block-causal and staircase) with the oracle.
 
-Small problems are compared element by element on every row; the full-size
-workloads on sampled rows (segment and block edges, the prefix/copy boundary
-and random rows) that the oracle computes one by one.
+Every comparison is element by element on every row and head: the small
+problems, the 4096-token prefill, the 8-trajectory staircase (one test per
+trajectory) and the 16-trajectory staircase (one test per trajectory, marked
+slow: about 12 TFLOP of dense fp64 oracle work in all).  A sampled-row check
+of the 16-trajectory workload (segment and block edges, the prefix/copy
+boundary and random rows) stays as the quick version of the last.
 """
 import numpy as np
 import pytest
@@ -47,6 +50,9 @@ SMALL = [
     ("single_token", [1, 1, 2], [0, 0, 0], 4, 4, 128, 32, "bf16"),
     ("f32_packed_gqa", [200, 57], [0, 0], 4, 2, 128, 16, "f32"),
     ("f32_staircase", [40 + 3 * 8], [3], 2, 1, 64, 8, "f32"),
+    # segments without copies packed next to staircase segments
+    ("mixed_S0_and_S", [96, 64 + 3 * 32, 128, 32 + 2 * 32, 45], [0, 3, 0, 2, 0], 8, 2, 128, 32,
+     "bf16"),
 ]
 
 
@@ -77,12 +83,45 @@ def sampled_check(w, seed):
     assert el <= TOL_BF16, el
 
 
-def test_prefill_4k_sampled():
-    sampled_check(W.prefill_bf16_4k(), 1)
+def test_prefill_4k_every_row():
+    full_check(W.prefill_bf16_4k(), TOL_BF16)
 
 
-def test_staircase_8traj_sampled():
-    sampled_check(W.staircase_fwd_8traj(), 3)
+_GPU_FWD = {}
+
+
+def gpu_forward(name, make):
+    """The GPU forward of a named workload, computed once per test module."""
+    if name not in _GPU_FWD:
+        w = make()
+        _GPU_FWD[name] = (w,) + run_fwd(w)
+    return _GPU_FWD[name]
+
+
+def segment_check(w, o, lse, s):
+    """Every row and head of segment s against the oracle run on that segment alone."""
+    a, b = int(w.cu_seqlens[s]), int(w.cu_seqlens[s + 1])
+    O, LSE = oracle.attention_fwd(w.q[a:b], w.k[a:b], w.v[a:b], [0, b - a], [int(w.s_copies[s])],
+                                  w.block_size, w.scale)
+    assert np.isfinite(o[a:b]).all() and np.isfinite(lse[:, a:b]).all()
+    eo, el = max_abs(o[a:b], O), max_abs(lse[:, a:b], LSE)
+    print(f"{w.name} segment {s} (L={b - a}, S={int(w.s_copies[s])}): max|dO| = {eo:.3g}, "
+          f"max|dLSE| = {el:.3g}")
+    assert eo <= TOL_BF16, eo
+    assert el <= TOL_BF16, el
+
+
+@pytest.mark.parametrize("s", range(8))
+def test_staircase_8traj_every_row(s):
+    w, o, lse = gpu_forward("8traj", W.staircase_fwd_8traj)
+    segment_check(w, o, lse, s)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("s", range(16))
+def test_staircase_16traj_every_row(s):
+    w, o, lse = gpu_forward("16traj", W.staircase_bwd_16traj)
+    segment_check(w, o, lse, s)
 
 
 def test_staircase_16traj_forward_sampled():
