@@ -28,7 +28,7 @@ EXPORTS = (
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
     "bca_staircase_groups_fwd", "bca_staircase_groups_bwd", "bca_decode_fp8",
-    "bca_staircase_bwd_stage",
+    "bca_staircase_bwd_stage", "bca_decode_noalloc",
 )
 
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_workspace.argtypes = [_I, _I, _I, _I, _I, _I]
     L.bca_decode.restype = _I
     L.bca_decode.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]
+    L.bca_decode_noalloc.restype = _I
+    L.bca_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]
     L.bca_decode_graph_create.restype = _I
     L.bca_decode_graph_create.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                           _S, _I, ctypes.POINTER(_P)]
@@ -406,6 +408,28 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
                           d, scale, _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
                           _stream(dev))
     _check("bca_decode", st)
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   scale: Optional[float] = None, num_splits: int = 0,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode step with the library's own per-GPU scratch (bca_decode_noalloc):
+    no workspace is allocated; pass ``out`` and ``lse`` to allocate nothing at
+    all.  Calls that overlap on one GPU race on the shared scratch."""
+    q_len, hq, kv_len, hkv, d = _decode_shapes("decode_noalloc", q, k, v, out, lse,
+                                               torch.bfloat16)
+    dev = _need_gpu(q, k, v, out, lse)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
+    st = lib().bca_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len,
+                                  hq, hkv, d, scale, _dtype_code(q), int(num_splits),
+                                  _stream(dev))
+    _check("bca_decode_noalloc", st)
     return out, lse
 
 

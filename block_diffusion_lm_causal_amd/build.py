@@ -29,6 +29,7 @@ SOURCES = [
     "attn_fwd_f32.hip",
     "attn_bwd_bf16.hip",
     "bca_util.hip",
+    "bca_scratch.hip",
 ]
 PROBE_SOURCES = ["probe.hip"]
 

@@ -506,6 +506,35 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(decode_enqueue(a, false, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
+bca_status_t bca_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                                float scale, bca_dtype_t dtype, int32_t num_splits,
+                                void* stream) {
+  g_last_error[0] = '\0';
+  const size_t need = bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits);
+  if (need > bca::kNoAllocScratchBytes)
+    return fail(BCA_ERR_WORKSPACE,
+                "this decode needs %zu bytes of scratch; the library holds %zu per device "
+                "(fewer splits or a caller workspace with bca_decode)",
+                need, bca::kNoAllocScratchBytes);
+  // Every argument check first (with a stand-in for the scratch address, so
+  // that a bad call never touches the HIP runtime), then the real address.
+  bca::DecodeArgs a{};
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+  bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
+                                num_splits, need > 0 ? stand_in : nullptr, need, &a);
+  if (st != BCA_OK) return st;
+  if (need > 0) {
+    void* scratch = nullptr;
+    st = hip_status(bca::noalloc_scratch(&scratch), "scratch address");
+    if (st != BCA_OK) return st;
+    st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype, num_splits,
+                     scratch, need, &a);
+    if (st != BCA_OK) return st;
+  }
+  return hip_status(decode_enqueue(a, false, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
 bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float k_scale,
                             float v_scale, void* o, float* lse, int32_t q_len, int32_t kv_len,
                             int32_t hq, int32_t hkv, int32_t d, float scale, int32_t num_splits,

@@ -97,6 +97,14 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t stream);
 // LSE * log2 e), 2 = dK/dV, 3 = dQ.
 hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, int stage, hipStream_t stream);
 
+// Bytes of the per-device scratch array behind bca_decode_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+// Device address of the calling thread's current device's scratch array
+// (fetched with hipGetSymbolAddress on the first call per device, then
+// cached).  Allocates nothing.
+hipError_t noalloc_scratch(void** ptr);
+
 // p[0 .. nwords) = value (a grid-stride fill kernel).
 hipError_t launch_fill_u32(void* p, size_t nwords, uint32_t value, hipStream_t stream);
 

@@ -248,6 +248,29 @@ bca_status_t bca_decode(const void* q, const void* k, const void* v, void* o, fl
                         size_t ws_bytes, void* stream);
 
 /*
+ * bca_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as bca_decode minus
+ * the workspace: the split partials go to a scratch array the library holds
+ * per GPU -- 32 MiB, allocated when the library's code is loaded on that GPU
+ * and kept until the process ends -- whose address is looked up on the first
+ * call on each device (that device must be current).  This call itself
+ * allocates and frees nothing.
+ *   - A call whose partials need more than 32 MiB
+ *     (bca_decode_workspace(q_len, kv_len, hq, hkv, d, num_splits) bytes)
+ *     returns BCA_ERR_WORKSPACE before anything is enqueued; ask for fewer
+ *     num_splits or use bca_decode with a workspace.
+ *   - All calls on one GPU share its scratch array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (several streams or
+ *     host threads with work in flight at once) race on it and may return
+ *     wrong results.  Order them on one stream, or use bca_decode.
+ * Nothing in the scratch array needs to start at zero.
+ */
+bca_status_t bca_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t d,
+                                float scale, bca_dtype_t dtype, int32_t num_splits, void* stream);
+
+/*
  * Decode step against an FP8 KV cache (the pages serve with an FP8 KV cache:
  * paper cards page, Table 11 configurations).  As bca_decode, except
  *   k8, v8            : [kv_len, hkv, d] bytes, OCP FP8 E4M3 (bias 7, no

@@ -188,3 +188,16 @@ def test_backward_stage_checks(L):
 def test_status_strings_cover_every_code(L):
     names = {L.bca_status_string(c) for c in range(7)}
     assert len(names) == 7 and b"unknown status" not in names
+
+
+def test_noalloc_decode_checks_before_touching_the_gpu(L):
+    def call(**kw):
+        a = dict(q=FAKE, q_len=32, kv_len=8224, hq=32, d=128, ns=0, dt=BF16)
+        a.update(kw)
+        return L.bca_decode_noalloc(a["q"], FAKE, FAKE, FAKE, FAKE, a["q_len"], a["kv_len"],
+                                    a["hq"], 8, a["d"], 0.088, a["dt"], a["ns"], None)
+    assert call(ns=256) == WS                       # 128 MiB of partials > 32 MiB held
+    assert b"scratch" in L.bca_last_error()
+    assert call(q_len=0) == SHAPE
+    assert call(d=96) == UNSUP
+    assert call(dt=F32) == DTYPE
