@@ -28,7 +28,8 @@ EXPORTS = (
     "bca_decode_graph_create", "bca_decode_graph_launch", "bca_decode_graph_destroy",
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
     "bca_staircase_groups_fwd", "bca_staircase_groups_bwd", "bca_decode_fp8",
-    "bca_staircase_bwd_stage", "bca_decode_noalloc",
+    "bca_staircase_bwd_stage", "bca_decode_noalloc", "bca_trajectory_cost_groups",
+    "bca_pack_balanced_groups",
 )
 
 
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.bca_trajectory_cost.argtypes = [_I, _I, _I]
     L.bca_pack_balanced.restype = _I
     L.bca_pack_balanced.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P]
+    L.bca_trajectory_cost_groups.restype = ctypes.c_int64
+    L.bca_trajectory_cost_groups.argtypes = [_I, _P, _P, _I, _I]
+    L.bca_pack_balanced_groups.restype = _I
+    L.bca_pack_balanced_groups.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]
     L.bca_pack_last_error.restype = ctypes.c_char_p
     L.bca_pack_last_error.argtypes = []
     _lib = L
@@ -537,4 +542,45 @@ def pack_balanced(seqlens, s_copies, block_size: int, nbins: int):
                                  vp(bin_cost), vp(order), vp(bin_start))
     if st != 0:
         raise BcaError("bca_pack_balanced", st, lib().bca_pack_last_error().decode())
+    return bin_of, bin_cost, order, bin_start
+
+
+def _group_arrays(groups):
+    """(group_start [n+1], group_pe, group_copies) int32 host arrays from a
+    list, per trajectory, of (pe, copies) groups."""
+    import numpy as np
+    start = np.zeros(len(groups) + 1, dtype=np.int32)
+    start[1:] = np.cumsum([len(g) for g in groups])
+    pe = np.ascontiguousarray([int(p) for g in groups for p, _ in g], dtype=np.int32)
+    cp = np.ascontiguousarray([int(c) for g in groups for _, c in g], dtype=np.int32)
+    return start, pe, cp
+
+
+def trajectory_cost_groups(seqlen: int, groups, block_size: int) -> int:
+    """Admitted pairs per query head of one general-staircase trajectory with
+    copy groups [(pe, copies), ...] (-1 if invalid)."""
+    _, pe, cp = _group_arrays([groups])
+    vp = lambda a: a.ctypes.data_as(_P) if a.size else None
+    return int(lib().bca_trajectory_cost_groups(int(seqlen), vp(pe), vp(cp), int(pe.size),
+                                                int(block_size)))
+
+
+def pack_balanced_groups(seqlens, groups, block_size: int, nbins: int):
+    """pack_balanced for general-staircase trajectories (copy groups per trajectory)."""
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    n = int(sl.shape[0])
+    if len(groups) != n:
+        raise BcaError("bca_pack_balanced_groups", 2, "one group list per trajectory")
+    start, pe, cp = _group_arrays(groups)
+    bin_of = np.zeros(n, dtype=np.int32)
+    bin_cost = np.zeros(max(int(nbins), 1), dtype=np.int64)
+    order = np.zeros(n, dtype=np.int32)
+    bin_start = np.zeros(max(int(nbins), 1) + 1, dtype=np.int32)
+    vp = lambda a: a.ctypes.data_as(_P) if a.size else None
+    st = lib().bca_pack_balanced_groups(vp(sl), vp(start), vp(pe), vp(cp), n, int(block_size),
+                                        int(nbins), vp(bin_of), vp(bin_cost), vp(order),
+                                        vp(bin_start))
+    if st != 0:
+        raise BcaError("bca_pack_balanced_groups", st, lib().bca_pack_last_error().decode())
     return bin_of, bin_cost, order, bin_start

@@ -54,12 +54,20 @@ __device__ __forceinline__ void wait_vmem_upto(int n) {
 template <int D>
 struct DecWave {
   int lane, half, wave, grp, wv, head, kv_head;
-  int split, kbeg, kend, ntile_all;  // this workgroup's key chunk
-  int qw0, qi;                       // first query row of the wave, the lane's row
-  bf16x8 qf[D / 16];                 // the lane's query, B operand of S^T = K Q^T
-  uint32_t koff[D / 16];             // K fragment offsets in a bf16 tile
-  uint32_t voff[D / 32][2];          // V^T transposed-read offsets in a bf16 tile
+  int split, ntile_all;  // this workgroup's split and its number of key tiles
+  int ntiles_kv;         // 64-key tiles of the whole cache
+  int qw0, qi;           // first query row of the wave, the lane's row
+  bf16x8 qf[D / 16];     // the lane's query, B operand of S^T = K Q^T
+  uint32_t koff[D / 16];     // K fragment offsets in a bf16 tile
+  uint32_t voff[D / 32][2];  // V^T transposed-read offsets in a bf16 tile
 };
+
+// Key tile i (0-based) of split `split`: tiles are dealt to the splits in
+// turn (split s takes tiles s, s + nsplit, s + 2 nsplit, ...), so at any
+// moment the workgroups of a KV head read one contiguous stretch of the cache.
+__device__ __forceinline__ int split_tile(int split, int nsplit, int i) {
+  return split + i * nsplit;
+}
 
 template <int D>
 __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& dw) {
@@ -79,13 +87,8 @@ __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& d
   dw.wv = dw.wave & 3;    // wave within its group
   dw.head = hg * a.hpw + dw.wv % a.hpw;
   dw.kv_head = (hg * a.hpw) / (a.hq / a.hkv);
-  // key tiles are dealt to the splits as evenly as they go
-  const int ntiles_kv = (a.kv_len + kBN - 1) / kBN;
-  const int t_first = (int)((long long)dw.split * ntiles_kv / a.nsplit);
-  const int t_end = (int)((long long)(dw.split + 1) * ntiles_kv / a.nsplit);
-  dw.kbeg = t_first * kBN;
-  dw.kend = min(a.kv_len, t_end * kBN);
-  dw.ntile_all = t_end - t_first;
+  dw.ntiles_kv = (a.kv_len + kBN - 1) / kBN;
+  dw.ntile_all = dw.split < dw.ntiles_kv ? (dw.ntiles_kv - dw.split + a.nsplit - 1) / a.nsplit : 0;
   dw.qw0 = tile * tok + (dw.wv / a.hpw) * kRows;
   dw.qi = dw.qw0 + (dw.lane & 31);
 #pragma unroll
@@ -223,21 +226,24 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
     return;
   }
   if (dw.qw0 >= a.q_len) return;  // a wave past the block's last query has no partial
-  // Partial of this (split, head, 32-token tile), normalised, in the
-  // accumulator's own layout: float4 (dt, g, lane) holds dims
-  // 32 dt + 8 g + 4 (lane / 32) + 0..3 of token lane % 32.  Every store
-  // instruction writes 1 KB contiguous.
+  // Partial of this (split, head, 32-token tile), normalised and rounded to
+  // bf16, in the accumulator's own layout: the 8-byte group (dt, g, lane)
+  // holds dims 32 dt + 8 g + 4 (lane / 32) + 0..3 of token lane % 32.  Every
+  // store instruction writes 512 bytes contiguous.  (The per-CU memory pipe
+  // sets the pace of this kernel, so the partial's bytes cost as much time as
+  // key/value bytes; the LSE stays float32.)
   const float l = xhalf_sum(ws.l);
   const float inv = 1.f / l;
   const int ntok32 = (a.q_len + kRows - 1) / kRows;
   const size_t ptile = ((size_t)dw.split * a.hq + dw.head) * ntok32 + dw.qw0 / kRows;
-  f32x4* po = reinterpret_cast<f32x4*>(a.part_o + ptile * (size_t)(kRows * D));
+  u32x2* po = reinterpret_cast<u32x2*>(a.part_o + ptile * (size_t)(kRows * D));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      po[(dt * 4 + gq) * 64 + lane] = f32x4{ws.acc[dt][4 * gq] * inv, ws.acc[dt][4 * gq + 1] * inv,
-                                            ws.acc[dt][4 * gq + 2] * inv, ws.acc[dt][4 * gq + 3] * inv};
+      po[(dt * 4 + gq) * 64 + lane] =
+          u32x2{pack_bf16x2(ws.acc[dt][4 * gq] * inv, ws.acc[dt][4 * gq + 1] * inv),
+                pack_bf16x2(ws.acc[dt][4 * gq + 2] * inv, ws.acc[dt][4 * gq + 3] * inv)};
     }
   }
   if (dw.half == 0) a.part_lse[ptile * kRows + (lane & 31)] = (ws.m + fast_log2(l)) * kLn2;
@@ -259,9 +265,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
 
   // This wave's loads of one tile: instructions wave + 8 j of the tile's
   // kInstPerTile (K blocks, then V blocks).
-  auto load_tile = [&](int t_round, int t_abs) {
-    const int k0 = dw.kbeg + t_abs * kBN;
-    const int rows = min(dw.kend - k0, kBN);
+  auto load_tile = [&](int t_round, int i) {
+    const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
+    const int rows = min(a.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * kv_elems * 2 + D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * kv_elems, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * kv_elems, nbytes);
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
       wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
       __syncthreads();
       dec_tile<D>(reinterpret_cast<const char*>(lds.k[t]), reinterpret_cast<const char*>(lds.v[t]),
-                  dw, dw.kbeg + (r0 + t) * kBN + 32 * dw.grp, dw.kend, a.scale_log2, ws);
+                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, a.kv_len,
+                  a.scale_log2, ws);
     }
   }
   __syncthreads();  // the tile buffers are free for the merge
@@ -329,9 +336,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   const uint8_t* kb = a.k8 + (size_t)dw.kv_head * D;
   const uint8_t* vb = a.v8 + (size_t)dw.kv_head * D;
 
-  auto load_tile = [&](int t_round, int t_abs) {
-    const int k0 = dw.kbeg + t_abs * kBN;
-    const int rows = min(dw.kend - k0, kBN);
+  auto load_tile = [&](int t_round, int i) {
+    const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
+    const int rows = min(a.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * row_bytes + D);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * row_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_bytes, nbytes);
@@ -385,7 +392,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
       widen(t);
       __syncthreads();  // bf16 pair complete
       dec_tile<D>(reinterpret_cast<const char*>(lds.k), reinterpret_cast<const char*>(lds.v),
-                  dw, dw.kbeg + (r0 + t) * kBN + 32 * dw.grp, dw.kend, a.scale_log2, ws);
+                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, a.kv_len,
+                  a.scale_log2, ws);
     }
   }
   __syncthreads();  // the tile buffers are free for the merge
@@ -403,25 +411,30 @@ constexpr int kCombineWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int kSlices = D / 8;  // 1 KB slices of a 32 x D fp32 partial
+  constexpr int kSlices = D / 8;  // 512-byte slices of a 32 x D bf16 partial
   constexpr int kChunk = 8;
   __shared__ f32x4 red_o[kCombineWaves][64];
   __shared__ float red_m[kCombineWaves][64], red_s[kCombineWaves][64];
   const int ntok32 = (a.q_len + 31) / 32;
-  const int slice = blockIdx.x % kSlices;
-  const int rest = blockIdx.x / kSlices;
+  // Workgroup order: head group fastest, as in the decode kernel, so that the
+  // partials of a head group are merged on the XCD whose L2 holds them.
+  const int ngroups = a.hq / a.hpw;
+  const int hg = blockIdx.x % ngroups;
+  int rest = blockIdx.x / ngroups;
+  const int slice = rest % kSlices;
+  rest /= kSlices;
   const int tile = rest % ntok32;
-  const int head = rest / ntok32;
+  const int head = hg * a.hpw + rest / ntok32;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row = lane & 31;
   const size_t tile_stride = (size_t)a.hq * ntok32;  // partial tiles per split
   const size_t my_tile = (size_t)head * ntok32 + tile;
   const float* lse_src = a.part_lse + my_tile * 32 + row;
-  const f32x4* o_src = reinterpret_cast<const f32x4*>(a.part_o + my_tile * (size_t)(32 * D)) +
+  const u32x2* o_src = reinterpret_cast<const u32x2*>(a.part_o + my_tile * (size_t)(32 * D)) +
                        slice * 64 + lane;
   const size_t lse_step = tile_stride * 32;             // floats between splits
-  const size_t o_step = tile_stride * (size_t)(8 * D);  // float4s between splits
+  const size_t o_step = tile_stride * (size_t)(8 * D);  // 8-byte groups between splits
   float m = kNegBig, sum = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = wave; c0 < a.nsplit; c0 += kChunk * kCombineWaves) {
@@ -434,7 +447,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(Deco
       y[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (c < a.nsplit) {
         x[u] = lse_src[(size_t)c * lse_step] * kLog2e;
-        y[u] = o_src[(size_t)c * o_step];
+        const u32x2 w2 = o_src[(size_t)c * o_step];
+        y[u] = f32x4{__uint_as_float(w2[0] << 16), __uint_as_float(w2[0] & 0xffff0000u),
+                     __uint_as_float(w2[1] << 16), __uint_as_float(w2[1] & 0xffff0000u)};
       }
     }
     float mc = m;

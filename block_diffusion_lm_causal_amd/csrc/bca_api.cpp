@@ -38,7 +38,7 @@ bca_status_t hip_status(hipError_t err, const char* what) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kPoisonWord = 0x7FC00000u;  // quiet NaN
+constexpr uint32_t kPoisonWord = 0x7FC07FC0u;  // a float32 NaN whose two halves are bf16 NaNs
 
 // An environment switch is on when set to anything but "" or "0".  Read at
 // every call, so a process may turn it on and off between calls.
@@ -388,25 +388,24 @@ bca_status_t bca_staircase_groups_bwd(const void* q, const void* k, const void* 
                   workspace, ws_bytes, 0, stream);
 }
 
-// Split-KV plan of the decode step: the 64-key tiles are dealt evenly to
-// the splits.  By default a split is one round of at most the 5 tiles a
-// workgroup stages in LDS, with at least 8 splits of 2 or more tiles for a
-// short cache, and no more workgroups than the 256 compute units while that
-// allows (a longer split is processed in rounds).
+// Split-KV plan of the decode step: the 64-key tiles are dealt to the splits
+// in turn.  By default: as few splits as give the smallest possible number of
+// tiles per split while one workgroup per split and KV head fits the 256
+// compute units.  Each CU streams its tiles at a fixed rate, so the kernel
+// lasts as long as its longest split, and fewer splits mean fewer partial
+// bytes to write and merge (129 tiles: 26 splits of at most 5 tiles, not 32
+// splits of which one has 5).
 static int decode_splits(int32_t q_len, int32_t kv_len, int32_t hq, int32_t hkv, int32_t req) {
   const int hpw = bca::heads_per_wg(hq, hkv);
   const int tok = 32 * (4 / hpw);
   const int ntok = (q_len + tok - 1) / tok;
   const int base_wgs = (hq / hpw) * ntok;
   const int tiles = (kv_len + 63) / 64;
-  int ns;
-  if (req > 0) {
-    ns = req;
-  } else {
-    ns = (tiles + 4) / 5;
-    if (ns < 8) ns = tiles / 2 < 8 ? tiles / 2 : 8;
-    const int cap = base_wgs < 256 ? 256 / base_wgs : 1;
-    if (ns > cap) ns = cap;
+  int ns = req;
+  if (req <= 0) {
+    const int ns_max = base_wgs < 256 ? 256 / base_wgs : 1;
+    const int per_split = (tiles + ns_max - 1) / ns_max;  // fewest tiles the longest split can have
+    ns = (tiles + per_split - 1) / per_split;
   }
   if (ns > tiles) ns = tiles;
   return ns < 1 ? 1 : ns;
@@ -420,8 +419,8 @@ size_t bca_decode_workspace(int32_t q_len, int32_t kv_len, int32_t hq, int32_t h
   const int ns = decode_splits(q_len, kv_len, hq, hkv, num_splits);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)ns * hq * ((q_len + 31) / 32) * 32;
-  const size_t po = (rows * d * sizeof(float) + 255) & ~(size_t)255;
-  const size_t pl = (rows * sizeof(float) + 255) & ~(size_t)255;
+  const size_t po = (rows * d * sizeof(uint16_t) + 255) & ~(size_t)255;  // bf16 partial O
+  const size_t pl = (rows * sizeof(float) + 255) & ~(size_t)255;          // float32 LSE
   return po + pl;
 }
 
@@ -457,8 +456,8 @@ static bca_status_t decode_args(const void* q, const void* k, const void* v, voi
   a->o = static_cast<uint16_t*>(o);
   a->lse = lse;
   const size_t po =
-      ((size_t)ns * hq * ((q_len + 31) / 32) * 32 * d * sizeof(float) + 255) & ~(size_t)255;
-  a->part_o = ns > 1 ? static_cast<float*>(workspace) : nullptr;
+      ((size_t)ns * hq * ((q_len + 31) / 32) * 32 * d * sizeof(uint16_t) + 255) & ~(size_t)255;
+  a->part_o = ns > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
   a->part_lse = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
   a->q_len = q_len;
   a->kv_len = kv_len;
@@ -479,7 +478,7 @@ static bca_status_t decode_args(const void* q, const void* k, const void* v, voi
 static hipError_t decode_enqueue(const bca::DecodeArgs& a, bool fp8, hipStream_t s) {
   if (a.nsplit > 1 && env_on("BCA_POISON")) {
     const size_t rows = (size_t)a.nsplit * a.hq * ((a.q_len + 31) / 32) * 32;
-    hipError_t err = bca::launch_fill_u32(a.part_o, rows * a.d, kPoisonWord, s);
+    hipError_t err = bca::launch_fill_u32(a.part_o, rows * a.d / 2, kPoisonWord, s);
     if (err == hipSuccess) err = bca::launch_fill_u32(a.part_lse, rows, kPoisonWord, s);
     if (err != hipSuccess) return err;
   }

@@ -49,9 +49,10 @@ struct DecodeArgs {
   uint16_t* o;        // [q_len, hq, d]
   float* lse;         // [hq, q_len]
   // Split partials (nsplit > 1), per (split, head, 32-token tile):
-  // part_o   [nsplit, hq, ceil(q_len/32), 32 * d] in the MFMA accumulator order
-  // part_lse [nsplit, hq, ceil(q_len/32), 32]
-  float* part_o;
+  // part_o   [nsplit, hq, ceil(q_len/32), 32 * d] bf16, normalised, in the MFMA
+  //          accumulator order
+  // part_lse [nsplit, hq, ceil(q_len/32), 32] float32
+  uint16_t* part_o;
   float* part_lse;
   int q_len, kv_len, hq, hkv, d, hpw;
   int nsplit;         // split s takes key tiles [s T / nsplit, (s + 1) T / nsplit), T = ceil(kv_len / 64)

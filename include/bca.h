@@ -349,6 +349,29 @@ bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, 
                                int32_t block_size, int32_t nbins, int32_t* bin_of,
                                int64_t* bin_cost, int32_t* order, int32_t* bin_start);
 
+/*
+ * The same for general trajectory staircases (copy groups, as in
+ * bca_staircase_groups_fwd).  Host arrays:
+ *   bca_trajectory_cost_groups: one trajectory of `seqlen` tokens with
+ *     `ngroups` groups (group_pe[g], group_copies[g]); its cost is the clean
+ *     prefix's B^2 n (n+1)/2 + r (n B + r) plus group_copies[g] * B *
+ *     (group_pe[g] + B) per group.  -1 for an invalid trajectory (a group's pe
+ *     not a multiple of B, outside [0, P] or decreasing, copies < 0, P < 0, or
+ *     P % B != 0 with copies).
+ *   bca_pack_balanced_groups: trajectory t owns groups
+ *     [group_start[t], group_start[t+1]) of group_pe / group_copies; outputs
+ *     and errors as bca_pack_balanced.
+ */
+int64_t bca_trajectory_cost_groups(int32_t seqlen, const int32_t* group_pe,
+                                   const int32_t* group_copies, int32_t ngroups,
+                                   int32_t block_size);
+
+bca_status_t bca_pack_balanced_groups(const int32_t* seqlens, const int32_t* group_start,
+                                      const int32_t* group_pe, const int32_t* group_copies,
+                                      int32_t ntraj, int32_t block_size, int32_t nbins,
+                                      int32_t* bin_of, int64_t* bin_cost, int32_t* order,
+                                      int32_t* bin_start);
+
 /* Message of the calling thread's last packing failure ("" if none). */
 const char* bca_pack_last_error(void);
 

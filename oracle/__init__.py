@@ -15,7 +15,8 @@ from .attention import (allowed_matrix, allowed_matrix_groups, attention_bwd,
                         attention_dq_rows, attention_fwd, decode, segment_allowed,
                         segment_prefix_len)
 from .fp8 import e4m3_to_float
-from .packing import lpt, optimal_makespan, trajectory_cost
+from .packing import lpt, optimal_makespan, trajectory_cost, trajectory_cost_groups
 
 __all__ = ["allowed_matrix", "allowed_matrix_groups", "segment_allowed", "attention_bwd", "attention_dq_rows", "attention_fwd", "decode",
-           "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost", "e4m3_to_float"]
+           "segment_prefix_len", "lpt", "optimal_makespan", "trajectory_cost", "trajectory_cost_groups",
+           "e4m3_to_float"]

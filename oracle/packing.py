@@ -16,12 +16,18 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import allowed_matrix
+from .attention import allowed_matrix, allowed_matrix_groups
 
 
 def trajectory_cost(seqlen: int, s_copies: int, block_size: int) -> int:
     """Admitted pairs of one trajectory, counted cell by cell from the mask."""
     return int(allowed_matrix(seqlen, s_copies, block_size).sum())
+
+
+def trajectory_cost_groups(seqlen: int, groups, block_size: int) -> int:
+    """Admitted pairs of one general-staircase trajectory (copy groups
+    [(pe, copies), ...]), counted cell by cell from its mask."""
+    return int(allowed_matrix_groups(seqlen, groups, block_size).sum())
 
 
 def lpt(costs, nbins: int):

@@ -115,7 +115,7 @@ def test_decode_workspace_and_checks(L):
     assert L.bca_decode_workspace(32, 1056, 32, 8, 128, 1) == 0
     assert L.bca_decode_workspace(32, 1056, 32, 8, 100, 0) == 0
     more = L.bca_decode_workspace(32, 8224, 32, 8, 128, 8)
-    assert more == 8 * 32 * 32 * 128 * 4 + 8 * 32 * 32 * 4
+    assert more == 8 * 32 * 32 * 128 * 2 + 8 * 32 * 32 * 4  # bf16 partial O, float32 LSE
     assert dec(L, FAKE, need - 1) == WS
     assert dec(L, None, need) == WS
     assert dec(L, FAKE, need, kv_len=16) == SHAPE       # kv_len < q_len
@@ -196,7 +196,7 @@ def test_noalloc_decode_checks_before_touching_the_gpu(L):
         a.update(kw)
         return L.bca_decode_noalloc(a["q"], FAKE, FAKE, FAKE, FAKE, a["q_len"], a["kv_len"],
                                     a["hq"], 8, a["d"], 0.088, a["dt"], a["ns"], None)
-    assert call(ns=256) == WS                       # 128 MiB of partials > 32 MiB held
+    assert call(ns=256) == WS                       # 64 MiB of partials > 32 MiB held
     assert b"scratch" in L.bca_last_error()
     assert call(q_len=0) == SHAPE
     assert call(d=96) == UNSUP

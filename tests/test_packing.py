@@ -101,6 +101,73 @@ def test_pack_rejects_bad_input():
         bca.pack_balanced([8], [0], 4, 0)        # no bins
 
 
+# --- copy-group trajectories ------------------------------------------------
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden",
+                                    "staircase_groups_allowed_L12_P6_B2.txt")
+
+
+def test_group_cost_counts_the_hand_written_table():
+    # The hand-written admitted-key table of a 12-token segment (groups
+    # (pe 2, 1 copy) and (pe 4, 2 copies), B = 2) lists 56 admitted pairs.
+    n = 0
+    for line in open(GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            n += len(line.split(":", 1)[1].split())
+    assert n == 56
+    assert oracle.trajectory_cost_groups(12, [(2, 1), (4, 2)], 2) == n
+    lib_or_skip()
+    assert bca.trajectory_cost_groups(12, [(2, 1), (4, 2)], 2) == n
+
+
+def random_groups(rng, n, B):
+    seqlens, groups = [], []
+    for _ in range(n):
+        nb = int(rng.integers(0, 7))
+        gs, pe = [], 0
+        for _ in range(int(rng.integers(0, 4))):
+            pe = int(rng.integers(pe // B, nb + 1)) * B   # non-decreasing, in [0, P]
+            gs.append((pe, int(rng.integers(0, 4))))
+        groups.append(gs)
+        seqlens.append(nb * B + B * sum(c for _, c in gs))
+    return seqlens, groups
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_cost_and_packing_match_the_oracle(seed):
+    lib_or_skip()
+    rng = np.random.default_rng(100 + seed)
+    B = 4
+    seqlens, groups = random_groups(rng, int(rng.integers(1, 12)), B)
+    costs = [oracle.trajectory_cost_groups(L, g, B) for L, g in zip(seqlens, groups)]
+    assert [bca.trajectory_cost_groups(L, g, B) for L, g in zip(seqlens, groups)] == costs
+    # one group seeing the whole prefix is the plain staircase
+    assert W.useful_pairs_groups(seqlens, groups, B) == sum(costs)
+    for m in (1, 2, 5):
+        got = bca.pack_balanced_groups(seqlens, groups, B, m)
+        want = oracle.lpt(costs, m)
+        for g, w_ in zip(got, want):
+            assert np.array_equal(g, w_), (seed, m)
+
+
+def test_one_group_is_the_plain_staircase_cost():
+    lib_or_skip()
+    for L, S, B in ((96, 2, 16), (40, 5, 8), (48, 6, 8)):
+        P = L - S * B
+        assert bca.trajectory_cost_groups(L, [(P, S)], B) == bca.trajectory_cost(L, S, B)
+
+
+def test_group_cost_rejects_bad_groups():
+    lib_or_skip()
+    assert bca.trajectory_cost_groups(12, [(3, 1)], 2) == -1          # pe not a multiple of B
+    assert bca.trajectory_cost_groups(12, [(4, 2), (2, 1)], 2) == -1  # pe decreasing
+    assert bca.trajectory_cost_groups(12, [(12, 1)], 2) == -1         # pe beyond P = 10
+    assert bca.trajectory_cost_groups(12, [(0, 7)], 2) == -1          # P < 0
+    assert bca.trajectory_cost_groups(12, [(0, -1)], 2) == -1         # negative copies
+    with pytest.raises(bca.BcaError):
+        bca.pack_balanced_groups([12, 8], [[(3, 1)], []], 2, 2)
+
+
 # --- a GPU consumer of the packed output ----------------------------------
 
 @pytest.mark.gpu
@@ -132,3 +199,41 @@ def test_packed_bins_reproduce_the_full_batch():
         torch.cuda.synchronize()
         assert torch.equal(o_b, o_all[idx])
         assert torch.equal(lse_b, lse_all[:, idx])
+
+
+@pytest.mark.gpu
+def test_packed_group_bins_reproduce_the_full_batch():
+    """The copy-group workload repacked into 3 bins by compute: each bin run
+    alone gives every trajectory bit-identical O, LSE, dQ, dK and dV rows."""
+    w = W.staircase_groups_8traj()
+    q, k, v, cu, _, do = device_inputs(w)
+    dev = q.device
+    gs, gp, gc = (torch.from_numpy(x).to(dev) for x in w.group_table())
+    B = w.block_size
+    o_all, lse_all = bca.staircase_groups_fwd(q, k, v, cu, gs, gp, gc, B, w.scale, w.max_seqlen)
+    g_all = bca.staircase_groups_bwd(q, k, v, o_all, lse_all, do, cu, gs, gp, gc, B, w.scale,
+                                     w.max_seqlen)
+    lens = np.diff(w.cu_seqlens)
+    bin_of, bin_cost, order, start = bca.pack_balanced_groups(lens, w.groups, B, 3)
+    costs = [oracle.trajectory_cost_groups(int(L), g, B) for L, g in zip(lens, w.groups)]
+    assert bin_cost.tolist() == oracle.lpt(costs, 3)[1].tolist()
+    for b in range(3):
+        members = order[start[b]:start[b + 1]].tolist()
+        if not members:
+            continue
+        rows = [torch.arange(int(w.cu_seqlens[t]), int(w.cu_seqlens[t + 1]), device=dev)
+                for t in members]
+        idx = torch.cat(rows)
+        cu_b = torch.tensor(np.concatenate([[0], np.cumsum([len(r) for r in rows])]),
+                            dtype=torch.int32, device=dev)
+        gs_b, gp_b, gc_b = (torch.from_numpy(x).to(dev)
+                            for x in bca._group_arrays([w.groups[t] for t in members]))
+        ml = max(len(r) for r in rows)
+        qb, kb, vb, dob = (t[idx].contiguous() for t in (q, k, v, do))
+        o_b, lse_b = bca.staircase_groups_fwd(qb, kb, vb, cu_b, gs_b, gp_b, gc_b, B, w.scale, ml)
+        g_b = bca.staircase_groups_bwd(qb, kb, vb, o_b, lse_b, dob, cu_b, gs_b, gp_b, gc_b, B,
+                                       w.scale, ml)
+        torch.cuda.synchronize()
+        assert torch.equal(o_b, o_all[idx]) and torch.equal(lse_b, lse_all[:, idx])
+        for x_b, x_all in zip(g_b, g_all):
+            assert torch.equal(x_b, x_all[idx]), b

@@ -50,7 +50,7 @@ def test_noalloc_rejects_more_than_its_scratch():
     q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
     o = torch.full_like(q, 3.0)
     lse = torch.full((w.hq, q.shape[0]), 3.0, device=dev)
-    # 256 splits of 32 heads x 32 rows x 128 floats: 128 MiB of partials
+    # 256 splits of 32 heads x 32 rows x 128 bf16 values: 64 MiB of partials
     assert noalloc_call(q, k, v, w.scale, o, lse, num_splits=256) == 5
     assert b"scratch" in bca.lib().bca_last_error()
     torch.cuda.synchronize()
