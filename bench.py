@@ -33,7 +33,7 @@ workload, plus bounded samples of every other workload (``per_config``), on
 the host's BLAS threads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-cpu]
-       [--paths prefill,decode,staircase,groups,packing,peaks] [--skip-headline]
+       [--paths prefill,decode,staircase,groups,packing,peaks,decode_calls] [--skip-headline]
        [--copy-calibration]
 Prints exactly one JSON line on stdout.
 """
@@ -348,6 +348,24 @@ def bench_decode(prefix: int, probe: Probe, flush, flush_read, calls: int = 32, 
     return res
 
 
+def bench_decode_calls(prefix: int, flush, calls: int = 16):
+    """Only the flushed decode calls (bf16 cache), for counter runs."""
+    import torch
+    from block_diffusion_lm_causal_amd import bca, workloads
+    dev = torch.device("cuda", 0)
+    w = workloads.decode_step(prefix)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    kv_len = prefix + w.block_size
+    ws = torch.empty(max(bca.decode_workspace(w.block_size, kv_len, w.hq, w.hkv, w.d), 16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.hq, w.block_size), dtype=torch.float32, device=dev)
+    cold, _ = timed_calls(lambda: bca.decode(q, k, v, w.scale, workspace=ws, out=o, lse=lse),
+                          calls, 2, flush=flush)
+    return {"workload": w.name, "calls": calls,
+            "us_per_call_flushed_median": round(statistics.median(cold) * 1e3, 3)}
+
+
 def bench_staircase8(steps: int, warmup: int):
     import numpy as np
     import torch
@@ -611,7 +629,7 @@ def main() -> int:
     bca.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda", 0)
     extra = set(p for p in args.paths.split(",") if p)
-    probe = Probe() if extra & {"decode", "peaks"} else None
+    probe = Probe() if extra & {"decode", "decode_calls", "peaks"} else None
     flush = flush_read = None
     if probe is not None:
         _flush_buf, flush_read = make_flush(dev, probe)
@@ -660,6 +678,10 @@ def main() -> int:
     if "prefill" in extra:
         log("[bench] block-causal prefill forward, 4096 tokens")
         paths["prefill_L4096"] = bench_prefill(max(args.steps, 20), args.warmup)
+    if "decode_calls" in extra:  # flushed calls only (short runs under the profilers)
+        for P in (1024, 8192):
+            log(f"[bench] decode P={P}, flushed calls only")
+            paths[f"decode_P{P}_calls"] = bench_decode_calls(P, flush)
     if "decode" in extra:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")
