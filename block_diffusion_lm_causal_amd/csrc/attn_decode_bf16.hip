@@ -119,22 +119,26 @@ __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& d
   }
 }
 
-// One 64-key bf16 tile (K at kt, V at vt) for this wave's key half: S^T in
-// two accumulator chains, mask past the chunk end, online softmax with the
-// lazy rescale, O^T += V^T P^T.  k0 is the first key of the half.
-template <int D>
-__device__ __forceinline__ void dec_tile(const char* kt, const char* vt, const DecWave<D>& dw,
-                                         int k0, int kend, float scale_log2, WaveState<D>& ws) {
+// One 64-key tile for this wave's key half: S^T in two accumulator chains,
+// mask past the cache end, online softmax with the lazy rescale, O^T +=
+// V^T P^T.  k0 is the first key of the half.  The MFMA A operands come from
+// the fetchers: kfrag(kk) the K fragment of dims 16 kk.. (keys on M), vfrag(c,
+// dt) the V^T fragment of dims 32 dt.. and keys 16 c.. of the half (dims on M),
+// each eight bf16 values per lane in the 32x32x16 operand layout.
+template <int D, typename KFrag, typename VFrag>
+__device__ __forceinline__ void dec_tile_with(KFrag kfrag, VFrag vfrag, const DecWave<D>& dw,
+                                              int k0, int kend, float scale_log2,
+                                              WaveState<D>& ws) {
   f32x16 s = f32x16{}, s1 = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < D / 16; kk += 2) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + dw.koff[kk]);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + dw.koff[kk + 1]);
+    const bf16x8 a0 = kfrag(kk);
+    const bf16x8 a1 = kfrag(kk + 1);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, dw.qf[kk], s, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, dw.qf[kk + 1], s1, 0, 0, 0);
   }
   s += s1;
-  if (k0 + 32 > kend) {  // keys past the chunk's end (zero-filled) are masked
+  if (k0 + 32 > kend) {  // keys past the cache's end (zero-filled) are masked
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = k0 + 8 * (r >> 2) + 4 * dw.half + (r & 3);
@@ -173,13 +177,22 @@ __device__ __forceinline__ void dec_tile(const char* kt, const char* vt, const D
   for (int c = 0; c < 2; ++c) {
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vt + dw.voff[dt][0] + c * 16 * D * 2));
-      const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vt + dw.voff[dt][1] + c * 16 * D * 2));
-      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, ws.acc[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < D / 32; ++dt)
+      ws.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(c, dt), pb, ws.acc[dt], 0, 0, 0);
   }
+}
+
+// The tile body on a bf16 tile pair (K at kt, V at vt, row-major, swizzled).
+template <int D>
+__device__ __forceinline__ void dec_tile(const char* kt, const char* vt, const DecWave<D>& dw,
+                                         int k0, int kend, float scale_log2, WaveState<D>& ws) {
+  auto kfrag = [&](int kk) { return *reinterpret_cast<const bf16x8*>(kt + dw.koff[kk]); };
+  auto vfrag = [&](int c, int dt) {
+    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vt + dw.voff[dt][0] + c * 16 * D * 2));
+    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vt + dw.voff[dt][1] + c * 16 * D * 2));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  dec_tile_with<D>(kfrag, vfrag, dw, k0, kend, scale_log2, ws);
 }
 
 // End of a decode workgroup: group B's (max, sum, O) merge into group A's
@@ -306,21 +319,41 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
 }
 
 // FP8 K/V cache (OCP E4M3; the pages run their decode with an FP8 KV cache,
-// paper cards page, Table 11 configurations).  Up to kDec8Tiles 64-key tiles
-// of raw bytes are requested at once (half the bytes of bf16); each tile,
-// once landed, is widened exactly to bf16 (v_cvt_pk_f32_fp8, then bf16
-// packing: every E4M3 value is a bf16 value) into one bf16 K/V tile pair
-// shared by the workgroup, and attended as in the bf16 kernel.  The K scale
-// is folded into scale_log2 and the V scale into o_mul.
-constexpr int kDec8Tiles = 6;
+// paper cards page, Table 11 configurations).  The E4M3 bytes of up to
+// kDec8Tiles 64-key tiles per round go to LDS (half the bytes of bf16) and
+// every wave widens its own operand fragments in registers right before its
+// MFMAs: K rows with an 8-byte LDS read, V^T with the transposed byte read
+// (ds_read_b64_tr_b8), then v_cvt_pk_f32_fp8 and bf16 packing -- exact, since
+// every E4M3 value is a bf16 value.  The K scale is folded into scale_log2
+// and the V scale into o_mul.
+constexpr int kDec8Tiles = 5;
 
 template <int D>
 struct LdsDec8 {
   uint8_t k8[kDec8Tiles][kBN * D];
   uint8_t v8[kDec8Tiles][kBN * D];
-  uint16_t k[kBN * D];
-  uint16_t v[kBN * D];
 };
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// 16-byte chunk swizzle of an E4M3 tile (D / 16 chunks of a D-byte row): the
+// 8-byte K reads of 32 rows at one logical chunk and the transposed reads of
+// 8 rows at one chunk spread over the LDS banks.
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  return (row >> 1) & (D / 16 - 1);
+}
+
+// Eight E4M3 bytes (in byte order) to eight bf16 values.
+__device__ __forceinline__ bf16x8 widen_e4m3x8(i32x2 raw) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(raw[1], true);
+  return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]),
+                                          pack_bf16x2(c[0], c[1]), pack_bf16x2(d[0], d[1])});
+}
 
 template <int D>
 __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
@@ -335,7 +368,41 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   const int row_bytes = a.hkv * D;
   const uint8_t* kb = a.k8 + (size_t)dw.kv_head * D;
   const uint8_t* vb = a.v8 + (size_t)dw.kv_head * D;
+  const int lane = dw.lane;
+  // K fragment kk: row 32 grp + lane % 32, bytes 16 kk + 8 (lane / 32) .. +8.
+  uint32_t koff8[D / 16];
+  {
+    const int R = 32 * dw.grp + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      koff8[kk] = (uint32_t)(R * D + ((kk ^ swz8<D>(R)) * 16) + 8 * dw.half);
+  }
+  // V^T fragment (c, dt) through the transposed byte read: in each 16-lane
+  // group g = lane / 16, address-lane 2 r + q points at 8 bytes (dims +8 q)
+  // of one key row, and lane i of the group receives byte i of the group's
+  // 16-byte segment from each of its 8 rows, in row order.  The rows are
+  // the keys the P operand pairs with element r of this lane: from the S^T
+  // accumulator layout, keys 16 c + 4 h + 0..3 and 16 c + 8 + 4 h + 0..3 of
+  // the half (h = lane / 32 = g / 2); the dims are 32 dt + 16 (g % 2) + i.
+  uint32_t voff8[2][D / 32];
+  {
+    const int g = (lane >> 4) & 3, i = lane & 15, r = i >> 1, q = i & 1;
+    const int kr = (r < 4 ? 0 : 8) + 4 * (g >> 1) + (r & 3);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int R = 32 * dw.grp + 16 * c + kr;
+        const int chunk = 2 * dt + (g & 1);
+        voff8[c][dt] = (uint32_t)(R * D + ((chunk ^ swz8<D>(R)) * 16) + 8 * q);
+      }
+    }
+  }
 
+  // This wave's loads of one tile: instructions wave + 8 j of the tile's
+  // kInstPerTile (K blocks, then V blocks); lane l of an instruction fills
+  // physical chunk l % kChunks8 of its row with the logical chunk the
+  // swizzle puts there.
   auto load_tile = [&](int t_round, int i) {
     const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
     const int rows = min(a.kv_len - k0, kBN);
@@ -344,37 +411,13 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_bytes, nbytes);
 #pragma unroll
     for (int j = 0; j < kInstPerWaveTile; ++j) {
-      const int i = dw.wave + 8 * j;
-      const bool is_k = i < kInstPerTile / 2;
-      const int row0 = (is_k ? i : i - kInstPerTile / 2) * kRowsPerInst;
-      const int R = row0 + dw.lane / kChunks8;
-      const uint32_t voff = (uint32_t)(R * row_bytes + (dw.lane % kChunks8) * 16);
+      const int ii = dw.wave + 8 * j;
+      const bool is_k = ii < kInstPerTile / 2;
+      const int row0 = (is_k ? ii : ii - kInstPerTile / 2) * kRowsPerInst;
+      const int R = row0 + lane / kChunks8;
+      const uint32_t voff = (uint32_t)(R * row_bytes + (((lane % kChunks8) ^ swz8<D>(R)) * 16));
       if (is_k) buffer_load_lds16(rk, lds.k8[t_round] + row0 * D, voff);
       else buffer_load_lds16(rv, lds.v8[t_round] + row0 * D, voff);
-    }
-  };
-  // Widen fp8 tile t to the bf16 tile pair: 16-byte chunk c of a tensor is
-  // dims 16 (c % kChunks8) .. +15 of row c / kChunks8, written as the two
-  // swizzled bf16 chunks of those dims.
-  auto widen = [&](int t) {
-    for (int ci = threadIdx.x; ci < 2 * kBN * kChunks8; ci += kPPThreads) {
-      const bool is_k = ci < kBN * kChunks8;
-      const int c = is_k ? ci : ci - kBN * kChunks8;
-      const int R = c / kChunks8, c16 = c % kChunks8;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>((is_k ? lds.k8[t] : lds.v8[t]) + R * D + c16 * 16);
-      uint32_t outw[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[e], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[e], true);
-        outw[2 * e] = pack_bf16x2(lo[0], lo[1]);
-        outw[2 * e + 1] = pack_bf16x2(hi[0], hi[1]);
-      }
-      char* dst = reinterpret_cast<char*>(is_k ? lds.k : lds.v) + R * D * 2;
-      *reinterpret_cast<u32x4*>(dst + (((2 * c16) ^ swz<D>(R)) * 16)) =
-          u32x4{outw[0], outw[1], outw[2], outw[3]};
-      *reinterpret_cast<u32x4*>(dst + (((2 * c16 + 1) ^ swz<D>(R)) * 16)) =
-          u32x4{outw[4], outw[5], outw[6], outw[7]};
     }
   };
 
@@ -385,15 +428,21 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   ws.l = 0.f;
   for (int r0 = 0; r0 < dw.ntile_all; r0 += kDec8Tiles) {
     const int nt = min(kDec8Tiles, dw.ntile_all - r0);
+    if (r0 > 0) __syncthreads();  // the previous round's tiles have been consumed
     for (int t = 0; t < nt; ++t) load_tile(t, r0 + t);
     for (int t = 0; t < nt; ++t) {
       wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
-      __syncthreads();  // fp8 tile t landed; the bf16 pair is no longer read
-      widen(t);
-      __syncthreads();  // bf16 pair complete
-      dec_tile<D>(reinterpret_cast<const char*>(lds.k), reinterpret_cast<const char*>(lds.v),
-                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, a.kv_len,
-                  a.scale_log2, ws);
+      __syncthreads();  // tile t has landed for every wave
+      const char* kt = reinterpret_cast<const char*>(lds.k8[t]);
+      const char* vt = reinterpret_cast<const char*>(lds.v8[t]);
+      auto kfrag = [&](int kk) {
+        return widen_e4m3x8(*reinterpret_cast<const i32x2*>(kt + koff8[kk]));
+      };
+      auto vfrag = [&](int c, int dt) {
+        return widen_e4m3x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + voff8[c][dt])));
+      };
+      dec_tile_with<D>(kfrag, vfrag, dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp,
+                       a.kv_len, a.scale_log2, ws);
     }
   }
   __syncthreads();  // the tile buffers are free for the merge
