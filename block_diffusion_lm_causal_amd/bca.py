@@ -29,7 +29,7 @@ EXPORTS = (
     "bca_trajectory_cost", "bca_pack_balanced", "bca_pack_last_error",
     "bca_staircase_groups_fwd", "bca_staircase_groups_bwd", "bca_decode_fp8",
     "bca_staircase_bwd_stage", "bca_decode_noalloc", "bca_trajectory_cost_groups",
-    "bca_pack_balanced_groups",
+    "bca_pack_balanced_groups", "bca_decode_loop_create",
 )
 
 
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_graph_create.restype = _I
     L.bca_decode_graph_create.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                           _S, _I, ctypes.POINTER(_P)]
+    L.bca_decode_loop_create.restype = _I
+    L.bca_decode_loop_create.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
+                                         _P, _S, _I, ctypes.POINTER(_P)]
     L.bca_decode_graph_launch.restype = _I
     L.bca_decode_graph_launch.argtypes = [_P, _P]
     L.bca_decode_graph_destroy.restype = None
@@ -514,6 +517,47 @@ class DecodeGraph:
             self.close()
         except Exception:
             pass
+
+
+class DecodeLoop(DecodeGraph):
+    """A denoising loop of ``steps`` decode calls captured once
+    (bca_decode_loop_create): step i reads q[i] and writes out[i], lse[i];
+    every step attends to the first ``kv_len_dev[0]`` rows of the k/v storage,
+    read on the GPU when the graph runs, so one graph serves every block."""
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 kv_len_dev: torch.Tensor, scale: Optional[float] = None, num_splits: int = 0,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None):
+        if q.dim() != 4:
+            raise BcaError("DecodeLoop", 2, "q must be [steps, q_len, hq, d]")
+        steps, q_len, hq, d = q.shape
+        _decode_shapes("DecodeLoop", q[0], k, v, None, None, torch.bfloat16)
+        _expect("DecodeLoop", q, "q", tuple(q.shape), torch.bfloat16)
+        _expect("DecodeLoop", out, "out", tuple(q.shape), torch.bfloat16)
+        _expect("DecodeLoop", lse, "lse", (steps, hq, q_len), torch.float32)
+        if kv_len_dev.dtype != torch.int32 or kv_len_dev.numel() < 1:
+            raise BcaError("DecodeLoop", 2, "kv_len_dev must be an int32 tensor")
+        dev = _need_gpu(q, k, v, kv_len_dev, workspace, out, lse)
+        kv_cap, hkv = k.shape[0], k.shape[1]
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        need = decode_workspace(q_len, kv_cap, hq, hkv, d, num_splits)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self.out = torch.empty_like(q) if out is None else out
+        self.lse = (torch.empty((steps, hq, q_len), dtype=torch.float32, device=dev)
+                    if lse is None else lse)
+        self._keep = (q, k, v, kv_len_dev, workspace)
+        self._dev = dev
+        self._handle = _P()
+        st = lib().bca_decode_loop_create(_ptr(q), _ptr(k), _ptr(v), _ptr(self.out),
+                                          _ptr(self.lse), _ptr(kv_len_dev), q_len, kv_cap, hq,
+                                          hkv, d, scale, _dtype_code(q), int(num_splits),
+                                          _ptr(workspace), ws_bytes, int(steps),
+                                          ctypes.byref(self._handle))
+        _check("bca_decode_loop_create", st)
+        self.steps = int(steps)
 
 
 def trajectory_cost(seqlen: int, s_copies: int, block_size: int) -> int:

@@ -55,6 +55,7 @@ template <int D>
 struct DecWave {
   int lane, half, wave, grp, wv, head, kv_head;
   int split, ntile_all;  // this workgroup's split and its number of key tiles
+  int kv_len;            // keys attended (the host's kv_len, or the device-resident length)
   int ntiles_kv;         // 64-key tiles of the whole cache
   int qw0, qi;           // first query row of the wave, the lane's row
   bf16x8 qf[D / 16];     // the lane's query, B operand of S^T = K Q^T
@@ -87,7 +88,12 @@ __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& d
   dw.wv = dw.wave & 3;    // wave within its group
   dw.head = hg * a.hpw + dw.wv % a.hpw;
   dw.kv_head = (hg * a.hpw) / (a.hq / a.hkv);
-  dw.ntiles_kv = (a.kv_len + kBN - 1) / kBN;
+  // The cache length: fixed at launch, or read from device memory (a
+  // captured loop whose prefix grows between replays), clamped to
+  // [q_len, kv_len] -- the grid and the partials were planned for kv_len.
+  dw.kv_len = a.kv_len;
+  if (a.kv_len_dev) dw.kv_len = min(max(*a.kv_len_dev, a.q_len), a.kv_len);
+  dw.ntiles_kv = (dw.kv_len + kBN - 1) / kBN;
   dw.ntile_all = dw.split < dw.ntiles_kv ? (dw.ntiles_kv - dw.split + a.nsplit - 1) / a.nsplit : 0;
   dw.qw0 = tile * tok + (dw.wv / a.hpw) * kRows;
   dw.qi = dw.qw0 + (dw.lane & 31);
@@ -245,8 +251,11 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
   // store instruction writes 512 bytes contiguous.  (The per-CU memory pipe
   // sets the pace of this kernel, so the partial's bytes cost as much time as
   // key/value bytes; the LSE stays float32.)
+  // A split with no keys (a device-resident cache length shorter than the
+  // plan) leaves l = 0: its partial is O = 0 with LSE = -inf, weight 0 in
+  // the merge.
   const float l = xhalf_sum(ws.l);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   const int ntok32 = (a.q_len + kRows - 1) / kRows;
   const size_t ptile = ((size_t)dw.split * a.hq + dw.head) * ntok32 + dw.qw0 / kRows;
   u32x2* po = reinterpret_cast<u32x2*>(a.part_o + ptile * (size_t)(kRows * D));
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
   // kInstPerTile (K blocks, then V blocks).
   auto load_tile = [&](int t_round, int i) {
     const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
-    const int rows = min(a.kv_len - k0, kBN);
+    const int rows = min(dw.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * kv_elems * 2 + D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * kv_elems, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * kv_elems, nbytes);
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
       wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
       __syncthreads();
       dec_tile<D>(reinterpret_cast<const char*>(lds.k[t]), reinterpret_cast<const char*>(lds.v[t]),
-                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, a.kv_len,
+                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, dw.kv_len,
                   a.scale_log2, ws);
     }
   }
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   // swizzle puts there.
   auto load_tile = [&](int t_round, int i) {
     const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
-    const int rows = min(a.kv_len - k0, kBN);
+    const int rows = min(dw.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * row_bytes + D);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * row_bytes, nbytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_bytes, nbytes);
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
         return widen_e4m3x8(__builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + voff8[c][dt])));
       };
       dec_tile_with<D>(kfrag, vfrag, dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp,
-                       a.kv_len, a.scale_log2, ws);
+                       dw.kv_len, a.scale_log2, ws);
     }
   }
   __syncthreads();  // the tile buffers are free for the merge

@@ -554,20 +554,13 @@ bca_status_t bca_decode_fp8(const void* q, const void* k8, const void* v8, float
   return hip_status(decode_enqueue(a, true, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
-bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,
-                                     float* lse, int32_t q_len, int32_t kv_len, int32_t hq,
-                                     int32_t hkv, int32_t d, float scale, bca_dtype_t dtype,
-                                     int32_t num_splits, void* workspace, size_t ws_bytes,
-                                     int32_t steps, bca_decode_graph_t** graph) {
-  g_last_error[0] = '\0';
-  if (!graph) return fail(BCA_ERR_NULL, "graph handle pointer is NULL");
-  *graph = nullptr;
-  if (steps < 1 || steps > kMaxGraphSteps)
-    return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
-  bca::DecodeArgs a{};
-  const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
-                                      num_splits, workspace, ws_bytes, &a);
-  if (st != BCA_OK) return st;
+}  // extern "C"
+
+// Record `steps` decode calls into a HIP graph through a private capture
+// stream and instantiate it: step i uses a0 with q, o and lse advanced by i
+// times the given element strides.
+static bca_status_t capture_decode(const bca::DecodeArgs& a0, int32_t steps, size_t q_step,
+                                   size_t o_step, size_t lse_step, bca_decode_graph_t** graph) {
   hipStream_t s = nullptr;
   hipError_t err = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
   if (err != hipSuccess) return hip_status(err, "capture stream");
@@ -577,8 +570,13 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
     return hip_status(err, "begin capture");
   }
   hipError_t launch_err = hipSuccess;
-  for (int32_t i = 0; i < steps && launch_err == hipSuccess; ++i)
+  for (int32_t i = 0; i < steps && launch_err == hipSuccess; ++i) {
+    bca::DecodeArgs a = a0;
+    a.q += (size_t)i * q_step;
+    a.o += (size_t)i * o_step;
+    a.lse += (size_t)i * lse_step;
     launch_err = decode_enqueue(a, false, s);
+  }
   hipGraph_t g = nullptr;
   err = hipStreamEndCapture(s, &g);
   (void)hipStreamDestroy(s);
@@ -594,6 +592,50 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
   }
   *graph = new bca_decode_graph{g, exec, steps};
   return BCA_OK;
+}
+
+extern "C" {
+
+bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int32_t q_len, int32_t kv_len, int32_t hq,
+                                     int32_t hkv, int32_t d, float scale, bca_dtype_t dtype,
+                                     int32_t num_splits, void* workspace, size_t ws_bytes,
+                                     int32_t steps, bca_decode_graph_t** graph) {
+  g_last_error[0] = '\0';
+  if (!graph) return fail(BCA_ERR_NULL, "graph handle pointer is NULL");
+  *graph = nullptr;
+  if (steps < 1 || steps > kMaxGraphSteps)
+    return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
+  bca::DecodeArgs a{};
+  const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_len, hq, hkv, d, scale, dtype,
+                                      num_splits, workspace, ws_bytes, &a);
+  if (st != BCA_OK) return st;
+  return capture_decode(a, steps, 0, 0, 0, graph);
+}
+
+bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int32_t* kv_len_dev, int32_t q_len,
+                                    int32_t kv_capacity, int32_t hq, int32_t hkv, int32_t d,
+                                    float scale, bca_dtype_t dtype, int32_t num_splits,
+                                    void* workspace, size_t ws_bytes, int32_t steps,
+                                    bca_decode_graph_t** graph) {
+  g_last_error[0] = '\0';
+  if (!graph) return fail(BCA_ERR_NULL, "graph handle pointer is NULL");
+  *graph = nullptr;
+  if (steps < 1 || steps > kMaxGraphSteps)
+    return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
+  if (!kv_len_dev) return fail(BCA_ERR_NULL, "kv_len_dev is NULL");
+  if ((reinterpret_cast<uintptr_t>(kv_len_dev) & 3u) != 0)
+    return fail(BCA_ERR_SHAPE, "kv_len_dev must be 4-byte aligned");
+  bca::DecodeArgs a{};
+  const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_capacity, hq, hkv, d, scale,
+                                      dtype, num_splits, workspace, ws_bytes, &a);
+  if (st != BCA_OK) return st;
+  if ((long long)steps * q_len * hq * d >= (1LL << 40))
+    return fail(BCA_ERR_SHAPE, "problem too large");
+  a.kv_len_dev = kv_len_dev;
+  const size_t qo_step = (size_t)q_len * hq * d;
+  return capture_decode(a, steps, qo_step, qo_step, (size_t)hq * q_len, graph);
 }
 
 bca_status_t bca_decode_graph_launch(bca_decode_graph_t* graph, void* stream) {

@@ -55,7 +55,11 @@ struct DecodeArgs {
   uint16_t* part_o;
   float* part_lse;
   int q_len, kv_len, hq, hkv, d, hpw;
-  int nsplit;         // split s takes key tiles [s T / nsplit, (s + 1) T / nsplit), T = ceil(kv_len / 64)
+  // Device-resident cache length (NULL: kv_len).  When set, the kernels
+  // attend to min(max(*kv_len_dev, q_len), kv_len) keys; kv_len is then the
+  // capacity the grid and the partials were planned for.
+  const int32_t* kv_len_dev;
+  int nsplit;         // split s takes key tiles s, s + nsplit, ... < T, T = ceil(kv_len / 64)
   float scale_log2;
 };
 

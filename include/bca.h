@@ -312,6 +312,34 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
                                      int32_t num_splits, void* workspace, size_t ws_bytes,
                                      int32_t steps, bca_decode_graph_t** graph);
 
+/*
+ * A block's whole denoising loop captured once and reused for every block
+ * of a generation (thread page, Result 4; the pages time one denoising round
+ * as the median over graph replays, paper cards page, Table 10 caption).  As
+ * bca_decode_graph_create, except that
+ *   q          : [steps, q_len, hq, d] bf16 -- step i reads q[i]
+ *   o, lse     : [steps, q_len, hq, d] bf16 and [steps, hq, q_len] float32 --
+ *                step i writes o[i], lse[i]
+ *   k, v       : [kv_capacity, hkv, d] bf16 cache storage
+ *   kv_len_dev : device int32, read by every step when the graph runs: the
+ *                number of cache rows attended (the prefix so far plus the
+ *                current block's own q_len rows, which are its last rows);
+ *                values outside [q_len, kv_capacity] are clamped into it
+ * The split plan and the workspace are those of bca_decode for kv_capacity
+ * keys (bca_decode_workspace(q_len, kv_capacity, ...)); splits that a
+ * shorter cache leaves empty contribute nothing.  The caller updates
+ * *kv_len_dev (and the cache rows, and q) between replays, with ordinary
+ * device work ordered before the launch.  Launch with
+ * bca_decode_graph_launch, release with bca_decode_graph_destroy.
+ * Errors as bca_decode_graph_create; kv_len_dev NULL: BCA_ERR_NULL.
+ */
+bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int32_t* kv_len_dev, int32_t q_len,
+                                    int32_t kv_capacity, int32_t hq, int32_t hkv, int32_t d,
+                                    float scale, bca_dtype_t dtype, int32_t num_splits,
+                                    void* workspace, size_t ws_bytes, int32_t steps,
+                                    bca_decode_graph_t** graph);
+
 bca_status_t bca_decode_graph_launch(bca_decode_graph_t* graph, void* stream);
 
 /* Releases the graph (NULL is ignored). */

@@ -84,3 +84,15 @@ def test_decode_checks():
     assert "v8" in expect(2, bca.decode_fp8, q, k8, k8[:, :, :64], 1.0, 1.0)
     expect(3, bca.decode_fp8, q.float(), k8, k8, 1.0, 1.0)
     assert "k must be" in expect(3, bca.DecodeGraph, q, k.float(), k, 4)
+
+
+def test_decode_loop_checks():
+    q = torch.zeros(4, 32, 8, 128, dtype=BF)
+    k = torch.zeros(288, 2, 128, dtype=BF)
+    n = torch.zeros(1, dtype=torch.int32)
+    expect(2, bca.DecodeLoop, q[0], k, k, n)                           # q needs a step axis
+    expect(3, bca.DecodeLoop, q.float(), k, k, n)
+    assert "v must have" in expect(2, bca.DecodeLoop, q, k, k[:, :, :64], n)
+    assert "out" in expect(2, bca.DecodeLoop, q, k, k, n, out=torch.zeros(32, 8, 128, dtype=BF))
+    assert "lse" in expect(2, bca.DecodeLoop, q, k, k, n, lse=torch.zeros(8, 32))
+    assert "kv_len_dev" in expect(2, bca.DecodeLoop, q, k, k, n.long())

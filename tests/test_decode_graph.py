@@ -58,3 +58,49 @@ def test_graph_launch_after_close_is_rejected():
     g.close()
     with pytest.raises(bca.BcaError):
         g.launch()
+
+
+def _oracle_check(q, k, v, scale, o, lse):
+    O, LSE = oracle.decode(q.cpu(), k.cpu(), v.cpu(), scale)
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    assert max_abs(o, O) <= TOL_BF16 and max_abs(lse, LSE) <= TOL_BF16
+
+
+# (requested splits, device-resident lengths written before successive replays):
+# full capacity, a shorter prefix, fewer tiles than splits (empty splits),
+# one ragged tile, and values clamped to [q_len, capacity].
+@pytest.mark.parametrize("num_splits", [16, 0])
+def test_loop_follows_the_device_resident_length(num_splits):
+    B, steps, cap = 32, 4, 2080
+    w = W.decode_step(cap - B, seed=21)
+    dev = torch.device("cuda", 0)
+    k, v = w.k.to(dev), w.v.to(dev)
+    rng = np.random.default_rng(22)
+    q = torch.from_numpy(rng.standard_normal((steps,) + tuple(w.q.shape), dtype=np.float32))
+    q = q.to(torch.bfloat16).to(dev)
+    kv_len = torch.full((1,), cap, dtype=torch.int32, device=dev)
+    loop = bca.DecodeLoop(q, k, v, kv_len, w.scale, num_splits=num_splits)
+    try:
+        for L in (2080, 1056, 544, 40, 5000, 10):
+            Lc = min(max(L, B), cap)
+            kv_len.fill_(L)
+            q.copy_(torch.from_numpy(rng.standard_normal(tuple(q.shape), dtype=np.float32)))
+            # the block's own rows are the last q_len rows of the attended cache
+            k[Lc - B:Lc].copy_(torch.from_numpy(
+                rng.standard_normal((B,) + tuple(k.shape[1:]), dtype=np.float32)))
+            torch.cuda.synchronize()
+            loop.launch()
+            torch.cuda.synchronize()
+            o_g, l_g = loop.out.clone(), loop.lse.clone()
+            for i in range(steps):
+                if num_splits and (Lc + 63) // 64 > 1:
+                    # same tiles per split (eager caps the split count at the
+                    # tile count; the loop's extra splits are empty, weight 0)
+                    o_e, l_e = bca.decode(q[i], k[:Lc], v[:Lc], w.scale, num_splits=num_splits)
+                    torch.cuda.synchronize()
+                    assert torch.equal(o_g[i], o_e), (L, i)
+                    assert torch.equal(l_g[i], l_e), (L, i)
+                _oracle_check(q[i], k[:Lc], v[:Lc], w.scale, o_g[i], l_g[i])
+    finally:
+        loop.close()
