@@ -341,6 +341,16 @@ def bench_decode(prefix: int, probe: Probe, flush, flush_read, calls: int = 32, 
         "us_512MB_read_alone_per_step": round(gread * 1e3, 2),
     }
     if not fp8:
+        # the captured loop with a device-resident cache length (one graph for
+        # every block of a generation), 32 steps per replay, caches warm
+        qs = q.unsqueeze(0).repeat(calls, 1, 1, 1).contiguous()
+        kv_len_dev = torch.full((1,), kv_len, dtype=torch.int32, device=dev)
+        loop = bca.DecodeLoop(qs, k, v, kv_len_dev, w.scale)
+        try:
+            per, _ = timed_calls(loop.launch, 10, 2)
+        finally:
+            loop.close()
+        res["us_per_step_device_len_loop_warm"] = round(statistics.median(per) * 1e3 / calls, 3)
         res["roofline_graph_cold"] = {
             "bound": "hbm", "achieved": gb(gcold * 1e3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(algo_bytes / (gcold * 1e3) / 1e3 / PEAK_HBM_GBS, 4),
