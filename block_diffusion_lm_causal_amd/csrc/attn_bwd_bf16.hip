@@ -16,14 +16,16 @@
 //      ("V waves", 32 keys each) compute S = Q K^T -> P and dV += P^T dO;
 //      waves 4-7 ("K waves", the same keys) compute dP = dO V^T, take P from
 //      their V wave through LDS, form dS and dK += dS^T Q.  S is computed
-//      once, and each SIMD pairs one wave of each kind, so one's MFMA work
-//      overlaps the other's exponentials.  K and V fragments and the dK/dV
-//      accumulators stay in registers; each step streams a 32-row tile of Q
-//      and dO (one query head) through LDS, loaded straight from HBM two steps
-//      ahead.  S is computed with queries on the M axis, so the P and dS
-//      accumulators are, unchanged, the A operands of the dV and dK products;
-//      their B operands (dO and Q with queries on K) come from the row-major
-//      tiles through the transposed LDS read.
+//      once, and each SIMD pairs one wave of each kind.  Each wave also
+//      issues its own elementwise work between its MFMAs: a V wave the
+//      exponentials of the next tile between its dV MFMAs, a K wave the dS
+//      of the current tile between the MFMAs of the next tile's dP.  K and V
+//      fragments and the dK/dV accumulators stay in registers; each step
+//      streams a 32-row tile of Q and dO (one query head) through LDS, loaded
+//      straight from HBM three steps ahead.  S is computed with queries on the
+//      M axis, so the P and dS accumulators are, unchanged, the A operands of
+//      the dV and dK products; their B operands (dO and Q with queries on K)
+//      come from the row-major tiles through the transposed LDS read.
 //   3. dQ: shaped like the forward's ping-pong kernel -- two groups of four
 //      waves, one phase apart, over 32-key tiles: MFMA phase S^T(t) = K Q^T,
 //      dP^T(t) = V dO^T and dQ^T += K^T dS^T(t-1); VALU phase P and dS of
@@ -119,6 +121,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   constexpr int kTileBytes = 2 * kQt * D * 2;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[4][2 * kQt * D];
   __shared__ KvSide lds;
+  __shared__ float side_spare[64];  // target of the zero-length side loads
   // P of a tile (bf16 pairs, two 16-byte words per lane) from each V wave to
   // the K wave of the same keys, double-buffered by step parity.
   __shared__ __attribute__((aligned(16))) uint32_t p_xchg[2][4][2][64 * 4];
@@ -196,29 +199,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   }
   // Steps sweep the query tiles of range 2, then of range 1, each from its
   // last tile down, every tile once per query head of the group.  A cursor
-  // holds the step's tile (first row), head within the group and range
-  // [lo, end); rows of a tile past `end` are loaded as zeros and masked.
+  // holds a step's tile t (in sweep order) and head h within the group; the
+  // tile's first row and the end of its range follow by selects, so the step
+  // loop has no data-dependent branches (a taken branch costs a SIMD about
+  // as much as several MFMA issue slots).  Rows of a tile past the end are
+  // loaded as zeros and masked.
   struct Cursor {
-    int qt0, h, lo, end;
+    int t, h;
   };
+  const int row0_r2 = qs2 + (nqt2 - 1) * kQt;         // tile t of range 2: row0_r2 - 32 t
+  const int row0_r1 = qs1 + (nqt1 - 1 + nqt2) * kQt;  // tile t of range 1: row0_r1 - 32 t
+  auto tile_row0 = [&](int t) { return (t < nqt2 ? row0_r2 : row0_r1) - t * kQt; };
+  auto tile_end = [&](int t) { return t < nqt2 ? qe2 : qe1; };
   auto advance = [&](Cursor& c) {
-    if (++c.h == group) {
-      c.h = 0;
-      c.qt0 -= kQt;
-      if (c.qt0 < c.lo && c.lo != qs1) {  // range 2 done: continue with range 1
-        c.qt0 = qs1 + (nqt1 - 1) * kQt;
-        c.lo = qs1;
-        c.end = qe1;
-      }
-    }
+    const int h1 = c.h + 1;
+    const bool wrap = h1 == group;
+    c.h = wrap ? 0 : h1;
+    c.t += wrap ? 1 : 0;
   };
   const uint32_t tiles_lds = lds_addr_of(&tiles[0][0]);
-  const uint32_t side_lds = lds_addr_of(&lds.v[0][0][0]);
-  auto issue_step = [&](const Cursor& c, int buf) {
-    const int qt0 = c.qt0;
+  // Side values: wave 0 loads the tile's LSE * log2(e) rows, wave 4 its delta
+  // rows, every other wave a zero-length load into a spare slot, so that all
+  // waves issue and wait for the same count.
+  const bool side_real = wave == 0 || wave == 4;
+  const float* const side_src = wave == 0 ? a.lse2 : a.delta;
+  const uint32_t side_dst = side_real ? lds_addr_of(&lds.v[0][wave == 0 ? 0 : 1][0])
+                                      : lds_addr_of(&side_spare[0]);
+  // A step past the last issues zero-length loads: they write zeros to a
+  // buffer that only steps past the last read.
+  auto issue_step = [&](const Cursor& c, int buf, bool valid) {
+    const int qt0 = valid ? tile_row0(c.t) : 0;
     const int head = g * group + c.h;
-    const int rows = min(c.end - qt0, kQt);
-    const uint32_t nbytes = (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2);
+    const int rows = valid ? min(tile_end(c.t) - qt0, kQt) : 0;
+    const uint32_t nbytes = rows > 0 ? (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2) : 0u;
     const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
@@ -228,19 +241,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
                            (uint32_t)(dma_row0[j] * D * 2);
       buffer_load_lds16_asm(r, dst, dma_voff[j]);
     }
-    if (wave == 0) {
-      const size_t so = (size_t)head * a.total + base + qt0;
-      const uint32_t sbytes = (uint32_t)(rows * 4);
-      const uint32_t dst = side_lds + (uint32_t)(buf * 2 * 64 * 4);
-      buffer_load_lds4_asm(rsrc_words(a.lse2 + so, sbytes), dst, (uint32_t)lane * 4);
-      buffer_load_lds4_asm(rsrc_words(a.delta + so, sbytes), dst + 64 * 4, (uint32_t)lane * 4);
-    }
+    const size_t so = (size_t)head * a.total + base + qt0;
+    const uint32_t sbytes = side_real ? (uint32_t)(rows * 4) : 0u;
+    buffer_load_lds4_asm(rsrc_words(side_src + so, sbytes),
+                         side_dst + (side_real ? (uint32_t)(buf * 2 * 64 * 4) : 0u),
+                         (uint32_t)lane * 4);
   };
   // Wait until only the newest step's loads may be outstanding.
-  auto wait_all_but_newest = [&]() {
-    if (wave == 0) wait_vmem_le<kDmaPerWave + 2>();
-    else wait_vmem_le<kDmaPerWave>();
-  };
+  auto wait_all_but_newest = [&]() { wait_vmem_le<kDmaPerWave + 1>(); };
 
   // K fragments of this wave's keys in V waves (B operand of S = Q K^T), V
   // fragments in K waves (B operand of dP = dO V^T).
@@ -257,9 +265,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       kvf[kk] = __builtin_bit_cast(bf16x8, r);
     }
   }
-  f32x16 acc[D / 32];  // dV (V waves) or dK (K waves): keys on M, dims on N
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
   // LDS offsets of this lane's fragments in a row-major swizzled tile, with
   // the tensor each role reads folded in: the A operand of S / dP comes from
@@ -309,53 +314,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
       f2hi = last.hi2;
     }
   }
+  // (bitwise & and |: short-circuit operators become branches)
+  auto active = [&](int qt0) {
+    return wave_has_keys &
+           (((qt0 < w1hi) & (qt0 + kQt > w1lo)) | ((qt0 < w2hi) & (qt0 + kQt > w2lo)));
+  };
 
-  // Steps are software-pipelined.  Tile t (a step's Q and dO rows with their
-  // side values) lives in buffer t % 4.  In step st the V waves compute
-  // dV += P(st)^T dO(st) from the P(st) they made one step earlier, and
-  // S(st+1) -> P(st+1), which they hand to the K waves through LDS; the K
-  // waves compute dP(st) = dO(st) V^T, dS(st) = P(st) (dP(st) - delta) and
-  // dK += dS(st)^T Q(st).  Each step ends with one barrier.  Tile st+3 is
-  // loaded into the buffer tile st-1 left; tile st+2 must have landed by the
-  // step's end.  The loop runs in groups of four steps (buffers and LDS
-  // offsets fixed at compile time, the handed-over P registers alternating);
-  // steps past the last do nothing.
-  Cursor cur = nqt2 > 0 ? Cursor{qs2 + (nqt2 - 1) * kQt, 0, qs2, qe2}
-                        : Cursor{qs1 + (nqt1 - 1) * kQt, 0, qs1, qe1};  // tile st
-  Cursor nx1 = cur;                                                     // tile st + 1
-  advance(nx1);
-  Cursor ld = cur;                                                      // next tile to load
-  // Prologue: tiles 0-2 issued, 0 and 1 landed.
-  if (nsteps > 0) {
-    issue_step(ld, 0);
-    advance(ld);
-    if (nsteps > 1) {
-      issue_step(ld, 1);
-      advance(ld);
-    }
-    if (nsteps > 2) {
-      issue_step(ld, 2);
-      advance(ld);
-    }
-  }
+  // Tiles: tile t (a step's Q and dO rows with their side values) lives in
+  // buffer t % 4; tiles 0-2 are loaded before the loop and step st loads
+  // tile st+3 into the buffer tile st-1 left.
+  Cursor ld = Cursor{0, 0};
+  issue_step(ld, 0, nsteps > 0);
+  advance(ld);
+  issue_step(ld, 1, nsteps > 1);
+  advance(ld);
+  issue_step(ld, 2, nsteps > 2);
+  advance(ld);
   // Everything landed, the K/V fragments included: the compiler does not
   // count the direct loads, so a partial wait here would leave it waiting
   // for those fragments (and with them every load in flight) inside the loop.
   wait_vmem();
   barrier_lds();
 
-  auto active = [&](const Cursor& c) {
-    return wave_has_keys &&
-           ((c.qt0 < w1hi && c.qt0 + kQt > w1lo) || (c.qt0 < w2hi && c.qt0 + kQt > w2lo));
-  };
-  // Side values of this lane's accumulator rows 8 r4 + 4 half + 0..3 of the
-  // tile in buffer `buf`: LSE * log2(e) (V waves) or delta (K waves).
-  auto read_side = [&](auto bc, int r4) {
-    constexpr int buf = decltype(bc)::value;
-    return *reinterpret_cast<const f32x4*>(&lds.v[buf][kwave ? 1 : 0][8 * r4 + 4 * half]);
-  };
-  // V waves: S = Q K^T of the tile in buffer `buf` (queries on M, keys on N).
-  // K waves: dP = dO V^T of the same tile.
+  // S = Q K^T (V waves) or dP = dO V^T (K waves) of the tile in buffer
+  // `buf`, queries on M, keys on N; A fragments read kQA MFMAs ahead of use
+  // (the scheduling groups pin that order; left alone, the compiler reads one
+  // ahead).
   auto qk_product = [&](auto bc) {
     constexpr int buf = decltype(bc)::value;
     uint32_t r0 = roff0;
@@ -363,9 +347,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     auto frag = [&](int kk) {
       return *reinterpret_cast<const bf16x8*>(tiles_c + buf * kTileBytes + (r0 ^ (32u * kk)));
     };
-    // fragments read kQA MFMAs ahead of use, so that LDS latency hides
-    // behind the MFMAs between; the scheduling groups below pin that order
-    // (left alone, the compiler reads one ahead)
     constexpr int kQA = 4;
     constexpr int kK = D / 16;
     __builtin_amdgcn_sched_barrier(0);
@@ -388,47 +369,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
     __builtin_amdgcn_sched_barrier(0);
     return sc;
   };
-  // V waves: P = exp2(S scale log2 e - LSE log2 e) over admitted (row, key)
-  // pairs, as bf16 pairs; register r of a lane holds query row 8(r/4) +
-  // 4 half + r%4 of the tile at cursor c.  In a tile not wholly admitted, a
-  // 32-bit row mask of this lane's key selects the pairs.
-  auto make_p = [&](const f32x16& sc, auto bc, const Cursor& c, uint32_t (&pk)[2][4]) {
-    const int qt0 = c.qt0, qe = c.end;
-    const bool full = qt0 + kQt <= qe && ((qt0 >= f1lo && qt0 + kQt <= f1hi) ||
-                                          (qt0 >= f2lo && qt0 + kQt <= f2hi));
-    auto rows = [&](bool masked, uint32_t m) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l2v = read_side(bc, r4);
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(fmaf(sc[4 * r4 + e], a.scale_log2, -l2v[e]));
-          v[e] = !masked || ((m >> (8 * r4 + e)) & 1u) ? pv : 0.f;
-        }
-        pk[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
-        pk[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
-      }
-    };
-    if (full) {
-      rows(false, 0u);
-    } else {
-      auto bits = [&](int lo, int hi) -> uint64_t {  // rows [lo, hi) of the tile
-        const int x = min(max(lo - qt0, 0), 32), y = min(max(hi - qt0, 0), 32);
-        return ((1ull << y) - 1) & ~((1ull << x) - 1);
-      };
-      const uint32_t m =
-          (uint32_t)((bits(kr.lo, kr.hi) | bits(kr.lo2, kr.hi2)) & bits(qt0, qe));
-      rows(true, m >> (4 * half));
-    }
-  };
   // acc += X^T Y over the tile's 32 query rows: X (keys on M, queries on K)
-  // from the P or dS registers, Y (queries on K, dims on N) from the
-  // row-major tile in buffer `buf` (dO or Q) through the transposed read.
-  auto accumulate = [&](const uint32_t (&pk)[2][4], auto bc) {
+  // from the P or dS words, Y (queries on K, dims on N) from the row-major
+  // tile in buffer `buf` (dO or Q) through the transposed read, its
+  // fragments read kAA MFMAs ahead.  chunk(j), j = 0..7, is VALU work
+  // independent of these MFMAs, issued in order behind them (8 / kM chunks
+  // after each MFMA; scheduling fences keep the order), so that it runs
+  // while the MFMA pipe is busy instead of after it.
+  auto accumulate = [&](f32x16 (&acc)[D / 32], const uint32_t (&xw)[2][4], auto bc,
+                        auto&& chunk) {
     constexpr int buf = decltype(bc)::value;
     constexpr int kM = 2 * (D / 32);  // MFMA m: c = m / (D/32), dt = m % (D/32)
-    constexpr int kAA = 3;        // B operands read kAA MFMAs ahead
+    constexpr int kAA = 3;
     auto frag = [&](int m) {
       const char* bt = tiles_c + buf * kTileBytes + (m / (D / 32)) * 16 * D * 2;
       return tr_pair(bt + toff[m % (D / 32)][0], bt + toff[m % (D / 32)][1]);
@@ -440,110 +392,185 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 #pragma unroll
     for (int m = 0; m < kM; ++m) {
       const int c = m / (D / 32), dt = m % (D / 32);
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]});
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, fr[m % kAA], acc[dt], 0, 0, 0);
+      const bf16x8 xa = __builtin_bit_cast(bf16x8, u32x4{xw[c][0], xw[c][1], xw[c][2], xw[c][3]});
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, fr[m % kAA], acc[dt], 0, 0, 0);
       if (m + kAA < kM) fr[m % kAA] = frag(m + kAA);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAA, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kM - kAA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int j = m * 8 / kM; j < (m + 1) * 8 / kM; ++j) chunk(j);  // 8 words in all
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kAA, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The side values of this lane's accumulator rows 8 r4 + 4 half + 0..3 of
+  // the tile in buffer `buf`: LSE * log2(e) (V waves) or delta (K waves).
+  auto read_side = [&](auto bc, int r4) {
+    constexpr int buf = decltype(bc)::value;
+    return *reinterpret_cast<const f32x4*>(&lds.v[buf][kwave ? 1 : 0][8 * r4 + 4 * half]);
+  };
+  // P of tile `c` from its scores (V waves): exp2(S scale log2(e) - LSE
+  // log2(e)) over admitted (row, key) pairs, bf16 pairs; register r of a
+  // lane holds query row 8(r/4) + 4 half + r%4.  A tile not wholly admitted
+  // selects the pairs with a 32-bit row mask of this lane's key; a tile
+  // that sees none of the wave's keys (or past the last step) gets P = 0.
+  // p_mask gives the mask, p_word(j) one packed word (registers 2j, 2j+1).
+  auto p_mask = [&](const Cursor& c, bool valid) -> uint32_t {
+    const int qt0 = tile_row0(c.t), qe = tile_end(c.t);
+    const bool act = valid & active(qt0);
+    const bool full = act & (qt0 + kQt <= qe) &
+                      (((qt0 >= f1lo) & (qt0 + kQt <= f1hi)) | ((qt0 >= f2lo) & (qt0 + kQt <= f2hi)));
+    auto bits = [&](int lo, int hi) -> uint64_t {  // rows [lo, hi) of the tile
+      const int x = min(max(lo - qt0, 0), 32), y = min(max(hi - qt0, 0), 32);
+      return ((1ull << y) - 1) & ~((1ull << x) - 1);
+    };
+    const uint32_t m = (uint32_t)((bits(kr.lo, kr.hi) | bits(kr.lo2, kr.hi2)) & bits(qt0, qe));
+    return full ? 0xffffffffu : (act ? m >> (4 * half) : 0u);
+  };
+  auto p_word = [&](const f32x16& sc, const f32x4 (&side)[4], uint32_t m, int j) {
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * j + e;
+      const float pv = fast_exp2(fmaf(sc[r], a.scale_log2, -side[r >> 2][r & 3]));
+      v[e] = ((m >> (8 * (r >> 2) + (r & 3))) & 1u) ? pv : 0.f;
+    }
+    return pack_bf16x2(v[0], v[1]);
   };
   uint32_t* const pex = &p_xchg[0][wave & 3][0][lane * 4];
   constexpr int kPexParity = 4 * 2 * 64 * 4;  // words between the two parities
-  auto put_p = [&](int parity, const uint32_t (&pk)[2][4]) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      *reinterpret_cast<u32x4*>(pex + parity * kPexParity + c * 64 * 4) =
-          u32x4{pk[c][0], pk[c][1], pk[c][2], pk[c][3]};
-  };
-  // P(st+1) (bf16 pairs) handed from a step to the next in V waves.
-  struct Carry {
-    uint32_t w[2][4];
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-
-  // Pre-step: P(0) (V waves, also handed over through LDS).
-  Carry carry_a = {}, carry_b = {};
-  if (nsteps > 0 && !kwave && active(cur)) {
-    const f32x16 sc = qk_product(I0{});
-    make_p(sc, I0{}, cur, carry_a.w);
-    put_p(0, carry_a.w);
-  }
-  barrier_lds();
-
-  auto step = [&](int st, auto bc, const Carry& cin, Carry& cout) {
-    constexpr int b = decltype(bc)::value;  // st % 4
-    using B1 = std::integral_constant<int, (b + 1) & 3>;
-    // Loads of tile st+3 into the buffer tile st-1 left, issued behind the
-    // first MFMAs of the step so that their issue overlaps the MFMA pipe.
-    auto issue = [&]() {
-      if (st + 3 < nsteps) {
-        issue_step(ld, (b + 3) & 3);
-        advance(ld);
-      }
-    };
-    const bool act = st < nsteps && active(cur);
-    const bool act1 = st + 1 < nsteps && active(nx1);
-    // V waves: S(st+1), then dV += P(st)^T dO(st), then P(st+1) (its
-    // exponentials overlap the dV products).  K waves: dP(st), dS(st) =
-    // P(st) (dP(st) - delta), then dK += dS(st)^T Q(st).  One accumulate
-    // for both roles keeps the accumulators in one set of registers.
-    f32x16 sc;  // S(st+1) or dP(st)
-    uint32_t xw[2][4];
-    if (!kwave) {
-      if (act1) sc = qk_product(B1{});
-      issue();
+  f32x16 acc[D / 32];  // dV (V waves) or dK (K waves): keys on M, dims on N
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xw[j >> 2][j & 3] = cin.w[j >> 2][j & 3];
-    } else if (act) {
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+
+  // The two roles run separate loops with one barrier per step each (the
+  // same count), so each keeps only its own live registers and its
+  // accumulator has one definition per step.  Steps past the last run the
+  // same code on zero P (their tiles are zero-length loads), which adds
+  // nothing.  The loops run in groups of four steps: buffer offsets are
+  // compile-time constants and the carried registers alternate.
+  if (!kwave) {
+    // V waves, step st: S(st+1) = Q(st+1) K^T; dV += P(st)^T dO(st) with the
+    // exponentials of P(st+1) between those MFMAs; P(st+1) to the K wave.
+    struct Carry {
+      uint32_t w[2][4];
+    };
+    Carry pa = {}, pb = {};
+    Cursor cur = Cursor{0, 0};  // tile st
+    {
+      const f32x16 sc = qk_product(I0{});
+      f32x4 side[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) side[r4] = read_side(I0{}, r4);
+      const uint32_t m = p_mask(cur, nsteps > 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pa.w[j >> 2][j & 3] = p_word(sc, side, m, j);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        *reinterpret_cast<u32x4*>(pex + c * 64 * 4) =
+            u32x4{pa.w[c][0], pa.w[c][1], pa.w[c][2], pa.w[c][3]};
+    }
+    barrier_lds();
+    auto step = [&](int st, auto bc, const Carry& pin, Carry& pout) {
+      constexpr int b = decltype(bc)::value;  // st % 4
+      using B1 = std::integral_constant<int, (b + 1) & 3>;
+      Cursor nx = cur;
+      advance(nx);
+      f32x4 side[4];  // read before the MFMAs they are scheduled among
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) side[r4] = read_side(B1{}, r4);
+      const f32x16 sc = qk_product(B1{});
+      issue_step(ld, (b + 3) & 3, st + 3 < nsteps);
+      advance(ld);
+      const uint32_t m = p_mask(nx, st + 1 < nsteps);
+      accumulate(acc, pin.w, bc,
+                 [&](int j) {
+                   uint32_t word = p_word(sc, side, m, j);
+                   asm volatile("" : "+v"(word));  // keep it among the MFMAs
+                   pout.w[j >> 2][j & 3] = word;
+                 });
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        *reinterpret_cast<u32x4*>(pex + ((b + 1) & 1) * kPexParity + c * 64 * 4) =
+            u32x4{pout.w[c][0], pout.w[c][1], pout.w[c][2], pout.w[c][3]};
+      cur = nx;
+      wait_all_but_newest();
+      barrier_lds();
+    };
+    for (int st = 0; st < nsteps; st += 4) {
+      step(st, I0{}, pa, pb);
+      step(st + 1, I1{}, pb, pa);
+      step(st + 2, I2{}, pa, pb);
+      step(st + 3, I3{}, pb, pa);
+    }
+  } else {
+    // K waves, step st: dP(st+1) = dO(st+1) V^T with dS(st) = P(st)
+    // (dP(st) - delta) between those MFMAs; dK += dS(st)^T Q(st).
+    f32x16 dpa = qk_product(I0{}), dpb = f32x16{};  // dP(0)
+    barrier_lds();
+    auto step = [&](int st, auto bc, const f32x16& dp_in, f32x16& dp_out) {
+      constexpr int b = decltype(bc)::value;
+      using B1 = std::integral_constant<int, (b + 1) & 3>;
       u32x4 pw[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
         pw[c] = *reinterpret_cast<const u32x4*>(pex + (b & 1) * kPexParity + c * 64 * 4);
-      sc = qk_product(bc);
-      issue();
+      f32x4 side[4];  // read before the MFMAs they are scheduled among
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 dlv = read_side(bc, r4);
-        const uint32_t w0 = pw[r4 >> 1][(r4 & 1) * 2 + 0];
-        const uint32_t w1 = pw[r4 >> 1][(r4 & 1) * 2 + 1];
-        const float p[4] = {bf16_to_f32(w0 & 0xffffu), bf16_to_f32(w0 >> 16),
-                            bf16_to_f32(w1 & 0xffffu), bf16_to_f32(w1 >> 16)};
-        float v[4];
+      for (int r4 = 0; r4 < 4; ++r4) side[r4] = read_side(bc, r4);
+      uint32_t xw[2][4];
+      // dP(st+1) MFMAs with dS(st) between them: after MFMA j, word j of
+      // dS(st) = P(st) (dP(st) - delta) (registers 2j, 2j+1)
+      {
+        uint32_t r0 = roff0;
+        asm volatile("" : "+v"(r0));
+        auto frag = [&](int kk) {
+          return *reinterpret_cast<const bf16x8*>(tiles_c + B1::value * kTileBytes +
+                                                  (r0 ^ (32u * kk)));
+        };
+        constexpr int kQA = 4;
+        constexpr int kK = D / 16;
+        static_assert(kK == 8 || kK == 4, "dS words per MFMA");
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 fr[kQA];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = p[e] * (sc[4 * r4 + e] - dlv[e]);
-        xw[r4 >> 1][(r4 & 1) * 2 + 0] = pack_bf16x2(v[0], v[1]);
-        xw[r4 >> 1][(r4 & 1) * 2 + 1] = pack_bf16x2(v[2], v[3]);
+        for (int i = 0; i < kQA; ++i) fr[i] = frag(i);
+        f32x16 dpn = f32x16{};
+        auto ds_word = [&](int j) {
+          const uint32_t w = pw[j >> 2][j & 3];
+          const float p0 = bf16_to_f32(w & 0xffffu), p1 = bf16_to_f32(w >> 16);
+          const int r = 2 * j;
+          const float v0 = p0 * (dp_in[r] - side[r >> 2][r & 3]);
+          const float v1 = p1 * (dp_in[r + 1] - side[(r + 1) >> 2][(r + 1) & 3]);
+          uint32_t word = pack_bf16x2(v0, v1);
+          asm volatile("" : "+v"(word));  // keep it here: IR passes sink it to its use
+          xw[j >> 2][j & 3] = word;
+        };
+#pragma unroll
+        for (int kk = 0; kk < kK; ++kk) {
+          dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[kk % kQA], kvf[kk], dpn, 0, 0, 0);
+          if (kk + kQA < kK) fr[kk % kQA] = frag(kk + kQA);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = kk * 8 / kK; j < (kk + 1) * 8 / kK; ++j) ds_word(j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        dp_out = dpn;
       }
-    } else {
-      issue();
+      issue_step(ld, (b + 3) & 3, st + 3 < nsteps);
+      advance(ld);
+      accumulate(acc, xw, bc, [](int) {});
+      wait_all_but_newest();
+      barrier_lds();
+    };
+    for (int st = 0; st < nsteps; st += 4) {
+      step(st, I0{}, dpa, dpb);
+      step(st + 1, I1{}, dpb, dpa);
+      step(st + 2, I2{}, dpa, dpb);
+      step(st + 3, I3{}, dpb, dpa);
     }
-    if (act) accumulate(xw, bc);
-    if (!kwave && act1) {
-      make_p(sc, B1{}, nx1, cout.w);
-      put_p((b + 1) & 1, cout.w);
-    }
-    advance(cur);
-    advance(nx1);
-    // Tile st+2 must have landed; tile st+3 stays in flight across the
-    // barrier.
-    if (st + 3 < nsteps) wait_all_but_newest();
-    else wait_vmem();
-    barrier_lds();
-  };
-  for (int st = 0; st < nsteps; st += 4) {
-    step(st, I0{}, carry_a, carry_b);
-    step(st + 1, I1{}, carry_b, carry_a);
-    step(st + 2, I2{}, carry_a, carry_b);
-    step(st + 3, I3{}, carry_b, carry_a);
   }
 
   // Epilogue: lane holds dims 32 dt + lane%32 of keys 8(r/4) + 4 half + r%4.
@@ -554,9 +581,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (kr < L) {
-        const size_t off = ((size_t)(base + kr) * a.hkv + g) * D + dt * 32 + (lane & 31);
+      const int kr2 = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (kr2 < L) {
+        const size_t off = ((size_t)(base + kr2) * a.hkv + g) * D + dt * 32 + (lane & 31);
         out[off] = static_cast<uint16_t>(pack_bf16x2(acc[dt][r] * mul, 0.f) & 0xffffu);
       }
     }
