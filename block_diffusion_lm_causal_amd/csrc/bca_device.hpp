@@ -71,8 +71,18 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t nbytes) {
 // that use these (the compiler reserves it, so it is listed only for the
 // reader).  The nops cover the write-to-use distances of the descriptor
 // SGPRs (when the compiler builds them with a VALU op) and of M0.
+// The descriptor and the LDS address are wave-uniform by construction; the
+// compiler may still hold such a value in a VGPR (a uniform select lowered to
+// v_cndmask), which an "s" operand cannot take, so every word goes through
+// readfirstlane (free when the value already sits in an SGPR).
+__device__ __forceinline__ i32x4 uniform_words(i32x4 r) {
+  return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
 __device__ __forceinline__ void buffer_load_lds16_asm(i32x4 r, uint32_t lds_addr,
                                                       uint32_t voffset) {
+  r = uniform_words(r);
+  lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
   asm volatile(
       "s_nop 4\n\t"
       "s_mov_b32 m0, %0\n\t"
@@ -84,6 +94,8 @@ __device__ __forceinline__ void buffer_load_lds16_asm(i32x4 r, uint32_t lds_addr
 }
 __device__ __forceinline__ void buffer_load_lds4_asm(i32x4 r, uint32_t lds_addr,
                                                      uint32_t voffset) {
+  r = uniform_words(r);
+  lds_addr = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr);
   asm volatile(
       "s_nop 4\n\t"
       "s_mov_b32 m0, %0\n\t"
