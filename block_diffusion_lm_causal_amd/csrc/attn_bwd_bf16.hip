@@ -121,7 +121,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   constexpr int kTileBytes = 2 * kQt * D * 2;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[4][2 * kQt * D];
   __shared__ KvSide lds;
-  __shared__ float side_spare[64];  // target of the zero-length side loads
   // P of a tile (bf16 pairs, two 16-byte words per lane) from each V wave to
   // the K wave of the same keys, double-buffered by step parity.
   __shared__ __attribute__((aligned(16))) uint32_t p_xchg[2][4][2][64 * 4];
@@ -219,12 +218,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
   };
   const uint32_t tiles_lds = lds_addr_of(&tiles[0][0]);
   // Side values: wave 0 loads the tile's LSE * log2(e) rows, wave 4 its delta
-  // rows, every other wave a zero-length load into a spare slot, so that all
-  // waves issue and wait for the same count.
+  // rows (every load instruction costs the issuing wave address-unit time, so
+  // the other waves issue none and wait for one load fewer).
   const bool side_real = wave == 0 || wave == 4;
   const float* const side_src = wave == 0 ? a.lse2 : a.delta;
-  const uint32_t side_dst = side_real ? lds_addr_of(&lds.v[0][wave == 0 ? 0 : 1][0])
-                                      : lds_addr_of(&side_spare[0]);
+  const uint32_t side_dst = lds_addr_of(&lds.v[0][wave == 0 ? 0 : 1][0]);
   // A step past the last issues zero-length loads: they write zeros to a
   // buffer that only steps past the last read.
   auto issue_step = [&](const Cursor& c, int buf, bool valid) {
@@ -241,14 +239,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
                            (uint32_t)(dma_row0[j] * D * 2);
       buffer_load_lds16_asm(r, dst, dma_voff[j]);
     }
-    const size_t so = (size_t)head * a.total + base + qt0;
-    const uint32_t sbytes = side_real ? (uint32_t)(rows * 4) : 0u;
-    buffer_load_lds4_asm(rsrc_words(side_src + so, sbytes),
-                         side_dst + (side_real ? (uint32_t)(buf * 2 * 64 * 4) : 0u),
-                         (uint32_t)lane * 4);
+    if (side_real) {
+      const size_t so = (size_t)head * a.total + base + qt0;
+      buffer_load_lds4_asm(rsrc_words(side_src + so, (uint32_t)(rows * 4)),
+                           side_dst + (uint32_t)(buf * 2 * 64 * 4), (uint32_t)lane * 4);
+    }
   };
   // Wait until only the newest step's loads may be outstanding.
-  auto wait_all_but_newest = [&]() { wait_vmem_le<kDmaPerWave + 1>(); };
+  auto wait_all_but_newest = [&]() {
+    if (side_real) wait_vmem_le<kDmaPerWave + 1>();
+    else wait_vmem_le<kDmaPerWave>();
+  };
 
   // K fragments of this wave's keys in V waves (B operand of S = Q K^T), V
   // fragments in K waves (B operand of dP = dO V^T).
