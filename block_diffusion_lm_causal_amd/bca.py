@@ -87,8 +87,8 @@ def lib() -> ctypes.CDLL:
     L.bca_decode_graph_create.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                           _S, _I, ctypes.POINTER(_P)]
     L.bca_decode_loop_create.restype = _I
-    L.bca_decode_loop_create.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I,
-                                         _P, _S, _I, ctypes.POINTER(_P)]
+    L.bca_decode_loop_create.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                                         _I, _P, _S, _I, ctypes.POINTER(_P)]
     L.bca_decode_graph_launch.restype = _I
     L.bca_decode_graph_launch.argtypes = [_P, _P]
     L.bca_decode_graph_destroy.restype = None
@@ -523,12 +523,14 @@ class DecodeLoop(DecodeGraph):
     """A denoising loop of ``steps`` decode calls captured once
     (bca_decode_loop_create): step i reads q[i] and writes out[i], lse[i];
     every step attends to the first ``kv_len_dev[0]`` rows of the k/v storage,
-    read on the GPU when the graph runs, so one graph serves every block."""
+    read on the GPU when the graph runs, so one graph serves every block.  With
+    ``steps_dev`` (int32 on the GPU) only the first ``steps_dev[0]`` steps of a
+    replay run; the others leave their outputs untouched."""
 
     def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  kv_len_dev: torch.Tensor, scale: Optional[float] = None, num_splits: int = 0,
                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 lse: Optional[torch.Tensor] = None):
+                 lse: Optional[torch.Tensor] = None, steps_dev: Optional[torch.Tensor] = None):
         if q.dim() != 4:
             raise BcaError("DecodeLoop", 2, "q must be [steps, q_len, hq, d]")
         steps, q_len, hq, d = q.shape
@@ -536,9 +538,10 @@ class DecodeLoop(DecodeGraph):
         _expect("DecodeLoop", q, "q", tuple(q.shape), torch.bfloat16)
         _expect("DecodeLoop", out, "out", tuple(q.shape), torch.bfloat16)
         _expect("DecodeLoop", lse, "lse", (steps, hq, q_len), torch.float32)
-        if kv_len_dev.dtype != torch.int32 or kv_len_dev.numel() < 1:
-            raise BcaError("DecodeLoop", 2, "kv_len_dev must be an int32 tensor")
-        dev = _need_gpu(q, k, v, kv_len_dev, workspace, out, lse)
+        for t, name in ((kv_len_dev, "kv_len_dev"), (steps_dev, "steps_dev")):
+            if t is not None and (t.dtype != torch.int32 or t.numel() < 1):
+                raise BcaError("DecodeLoop", 2, f"{name} must be an int32 tensor")
+        dev = _need_gpu(q, k, v, kv_len_dev, steps_dev, workspace, out, lse)
         kv_cap, hkv = k.shape[0], k.shape[1]
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
         need = decode_workspace(q_len, kv_cap, hq, hkv, d, num_splits)
@@ -548,11 +551,12 @@ class DecodeLoop(DecodeGraph):
         self.out = torch.empty_like(q) if out is None else out
         self.lse = (torch.empty((steps, hq, q_len), dtype=torch.float32, device=dev)
                     if lse is None else lse)
-        self._keep = (q, k, v, kv_len_dev, workspace)
+        self._keep = (q, k, v, kv_len_dev, steps_dev, workspace)
         self._dev = dev
         self._handle = _P()
         st = lib().bca_decode_loop_create(_ptr(q), _ptr(k), _ptr(v), _ptr(self.out),
-                                          _ptr(self.lse), _ptr(kv_len_dev), q_len, kv_cap, hq,
+                                          _ptr(self.lse), _ptr(kv_len_dev), _ptr(steps_dev),
+                                          q_len, kv_cap, hq,
                                           hkv, d, scale, _dtype_code(q), int(num_splits),
                                           _ptr(workspace), ws_bytes, int(steps),
                                           ctypes.byref(self._handle))

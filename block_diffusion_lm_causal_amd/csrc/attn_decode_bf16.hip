@@ -273,6 +273,7 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
 
 template <int D>
 __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
+  if (a.steps_dev && a.step >= *a.steps_dev) return;  // a step the loop skips
   __shared__ LdsDec<D> lds;
   constexpr int kChunks = D / 8;
   constexpr int kRowsPerInst = 64 / kChunks;
@@ -366,6 +367,7 @@ __device__ __forceinline__ bf16x8 widen_e4m3x8(i32x2 raw) {
 
 template <int D>
 __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
+  if (a.steps_dev && a.step >= *a.steps_dev) return;  // a step the loop skips
   __shared__ LdsDec8<D> lds;
   constexpr int kChunks8 = D / 16;                         // 16-byte chunks per fp8 row
   constexpr int kRowsPerInst = 64 / kChunks8;              // 8 (D=128) or 16 (D=64)
@@ -469,6 +471,7 @@ constexpr int kCombineWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void decode_combine_kernel(DecodeArgs a) {
+  if (a.steps_dev && a.step >= *a.steps_dev) return;  // a step the loop skips
   constexpr int kSlices = D / 8;  // 512-byte slices of a 32 x D bf16 partial
   constexpr int kChunk = 8;
   __shared__ f32x4 red_o[kCombineWaves][64];

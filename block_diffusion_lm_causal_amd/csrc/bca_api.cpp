@@ -572,6 +572,7 @@ static bca_status_t capture_decode(const bca::DecodeArgs& a0, int32_t steps, siz
   hipError_t launch_err = hipSuccess;
   for (int32_t i = 0; i < steps && launch_err == hipSuccess; ++i) {
     bca::DecodeArgs a = a0;
+    a.step = i;
     a.q += (size_t)i * q_step;
     a.o += (size_t)i * o_step;
     a.lse += (size_t)i * lse_step;
@@ -614,7 +615,8 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
 }
 
 bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v, void* o,
-                                    float* lse, const int32_t* kv_len_dev, int32_t q_len,
+                                    float* lse, const int32_t* kv_len_dev,
+                                    const int32_t* steps_dev, int32_t q_len,
                                     int32_t kv_capacity, int32_t hq, int32_t hkv, int32_t d,
                                     float scale, bca_dtype_t dtype, int32_t num_splits,
                                     void* workspace, size_t ws_bytes, int32_t steps,
@@ -625,8 +627,9 @@ bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v,
   if (steps < 1 || steps > kMaxGraphSteps)
     return fail(BCA_ERR_SHAPE, "steps must be in [1, %d] (got %d)", kMaxGraphSteps, steps);
   if (!kv_len_dev) return fail(BCA_ERR_NULL, "kv_len_dev is NULL");
-  if ((reinterpret_cast<uintptr_t>(kv_len_dev) & 3u) != 0)
-    return fail(BCA_ERR_SHAPE, "kv_len_dev must be 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kv_len_dev) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(steps_dev) & 3u) != 0)
+    return fail(BCA_ERR_SHAPE, "kv_len_dev and steps_dev must be 4-byte aligned");
   bca::DecodeArgs a{};
   const bca_status_t st = decode_args(q, k, v, o, lse, q_len, kv_capacity, hq, hkv, d, scale,
                                       dtype, num_splits, workspace, ws_bytes, &a);
@@ -634,6 +637,7 @@ bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v,
   if ((long long)steps * q_len * hq * d >= (1LL << 40))
     return fail(BCA_ERR_SHAPE, "problem too large");
   a.kv_len_dev = kv_len_dev;
+  a.steps_dev = steps_dev;
   const size_t qo_step = (size_t)q_len * hq * d;
   return capture_decode(a, steps, qo_step, qo_step, (size_t)hq * q_len, graph);
 }

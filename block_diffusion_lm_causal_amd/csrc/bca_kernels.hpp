@@ -59,6 +59,10 @@ struct DecodeArgs {
   // attend to min(max(*kv_len_dev, q_len), kv_len) keys; kv_len is then the
   // capacity the grid and the partials were planned for.
   const int32_t* kv_len_dev;
+  // Device-resident step count of a captured loop (NULL: every step runs):
+  // the launches of step `step` return at once when step >= *steps_dev.
+  const int32_t* steps_dev;
+  int step;
   int nsplit;         // split s takes key tiles s, s + nsplit, ... < T, T = ceil(kv_len / 64)
   float scale_log2;
 };

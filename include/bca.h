@@ -325,16 +325,22 @@ bca_status_t bca_decode_graph_create(const void* q, const void* k, const void* v
  *                number of cache rows attended (the prefix so far plus the
  *                current block's own q_len rows, which are its last rows);
  *                values outside [q_len, kv_capacity] are clamped into it
+ *   steps_dev  : device int32 or NULL: the number of steps a replay runs
+ *                (a block that stops denoising early); the kernels of
+ *                steps i >= *steps_dev return at once and leave o[i], lse[i]
+ *                as they were.  NULL: all `steps` run
  * The split plan and the workspace are those of bca_decode for kv_capacity
  * keys (bca_decode_workspace(q_len, kv_capacity, ...)); splits that a
  * shorter cache leaves empty contribute nothing.  The caller updates
  * *kv_len_dev (and the cache rows, and q) between replays, with ordinary
  * device work ordered before the launch.  Launch with
  * bca_decode_graph_launch, release with bca_decode_graph_destroy.
- * Errors as bca_decode_graph_create; kv_len_dev NULL: BCA_ERR_NULL.
+ * Errors as bca_decode_graph_create; kv_len_dev NULL: BCA_ERR_NULL; a pointer
+ * not 4-byte aligned: BCA_ERR_SHAPE.
  */
 bca_status_t bca_decode_loop_create(const void* q, const void* k, const void* v, void* o,
-                                    float* lse, const int32_t* kv_len_dev, int32_t q_len,
+                                    float* lse, const int32_t* kv_len_dev,
+                                    const int32_t* steps_dev, int32_t q_len,
                                     int32_t kv_capacity, int32_t hq, int32_t hkv, int32_t d,
                                     float scale, bca_dtype_t dtype, int32_t num_splits,
                                     void* workspace, size_t ws_bytes, int32_t steps,

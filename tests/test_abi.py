@@ -159,11 +159,12 @@ def test_decode_loop_checks(L):
     h = ctypes.c_void_p()
     need = L.bca_decode_workspace(32, 2080, 32, 8, 128, 0)
 
-    def create(steps=4, lenp=FAKE, cap=2080, ws=FAKE, handle=ctypes.byref(h)):
-        return L.bca_decode_loop_create(FAKE, FAKE, FAKE, FAKE, FAKE, lenp, 32, cap, 32, 8, 128,
-                                        0.088, BF16, 0, ws, need, steps, handle)
+    def create(steps=4, lenp=FAKE, stepsp=None, cap=2080, ws=FAKE, handle=ctypes.byref(h)):
+        return L.bca_decode_loop_create(FAKE, FAKE, FAKE, FAKE, FAKE, lenp, stepsp, 32, cap, 32,
+                                        8, 128, 0.088, BF16, 0, ws, need, steps, handle)
     assert create(lenp=None) == NULL and not h.value
     assert create(lenp=ctypes.c_void_p((1 << 20) + 2)) == SHAPE   # int32 alignment
+    assert create(stepsp=ctypes.c_void_p((1 << 20) + 2)) == SHAPE
     assert create(steps=0) == SHAPE
     assert create(steps=5000) == SHAPE
     assert create(cap=16) == SHAPE               # capacity below q_len

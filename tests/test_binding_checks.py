@@ -96,3 +96,4 @@ def test_decode_loop_checks():
     assert "out" in expect(2, bca.DecodeLoop, q, k, k, n, out=torch.zeros(32, 8, 128, dtype=BF))
     assert "lse" in expect(2, bca.DecodeLoop, q, k, k, n, lse=torch.zeros(8, 32))
     assert "kv_len_dev" in expect(2, bca.DecodeLoop, q, k, k, n.long())
+    assert "steps_dev" in expect(2, bca.DecodeLoop, q, k, k, n, steps_dev=n.float())

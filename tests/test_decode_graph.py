@@ -104,3 +104,34 @@ def test_loop_follows_the_device_resident_length(num_splits):
                 _oracle_check(q[i], k[:Lc], v[:Lc], w.scale, o_g[i], l_g[i])
     finally:
         loop.close()
+
+
+def test_loop_runs_the_device_resident_step_count():
+    """Only the first steps_dev[0] steps of a replay run; later steps leave
+    their outputs as they were (here NaN), and the steps that run equal a
+    replay of the whole loop."""
+    B, steps, cap = 32, 4, 1056
+    w = W.decode_step(cap - B, seed=23)
+    dev = torch.device("cuda", 0)
+    k, v = w.k.to(dev), w.v.to(dev)
+    rng = np.random.default_rng(24)
+    q = torch.from_numpy(rng.standard_normal((steps,) + tuple(w.q.shape), dtype=np.float32))
+    q = q.to(torch.bfloat16).to(dev)
+    kv_len = torch.full((1,), cap, dtype=torch.int32, device=dev)
+    n_steps = torch.full((1,), steps, dtype=torch.int32, device=dev)
+    loop = bca.DecodeLoop(q, k, v, kv_len, w.scale, steps_dev=n_steps)
+    try:
+        loop.launch()
+        torch.cuda.synchronize()
+        o_all, l_all = loop.out.clone(), loop.lse.clone()
+        for n in (2, 0, 3):
+            loop.out.fill_(float("nan"))
+            loop.lse.fill_(float("nan"))
+            n_steps.fill_(n)
+            torch.cuda.synchronize()
+            loop.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(loop.out[:n], o_all[:n]) and torch.equal(loop.lse[:n], l_all[:n])
+            assert torch.isnan(loop.out[n:].float()).all() and torch.isnan(loop.lse[n:]).all()
+    finally:
+        loop.close()
