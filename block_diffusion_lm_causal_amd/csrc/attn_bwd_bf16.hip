@@ -45,28 +45,47 @@ constexpr int kKvKeys = 128;  // keys per dK/dV workgroup
 // ---------------------------------------------------------------------------
 // 1. delta[h][i] = sum_d dO[i,h,d] * O[i,h,d], and lse2[h][i] = LSE[h][i] log2(e)
 
+// One workgroup takes kDeltaPasses x (256 / (d/8)) consecutive query rows of
+// one head (d/8 lanes per row, 16 bytes each), all loads issued before any
+// arithmetic so that every lane has 2 kDeltaPasses loads in flight; the rows
+// it writes are consecutive in the [hq, total] side arrays.  Workgroups are
+// ordered head fastest, so neighbouring workgroups read neighbouring bytes
+// of the token-major O and dO.
+constexpr int kDeltaPasses = 4;
+
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   const int d = a.d;
-  const int lanes_per_row = d / 8;  // 16 (d = 128) or 8 (d = 64)
-  const long long row = (long long)blockIdx.x * (256 / lanes_per_row) + threadIdx.x / lanes_per_row;
+  const int lanes_per_row = d / 8;                     // 16 (d = 128) or 8 (d = 64)
+  const int rows_per_pass = 256 / lanes_per_row;       // 16 or 32
+  const int h = (int)(blockIdx.x % (unsigned)a.hq);
+  const long long i0 = (long long)(blockIdx.x / (unsigned)a.hq) * rows_per_pass * kDeltaPasses;
   const int sub = threadIdx.x % lanes_per_row;
-  const long long nrows = (long long)a.total * a.hq;
-  float acc = 0.f;
-  if (row < nrows) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(a.o + row * d + sub * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + row * d + sub * 8);
+  const int r = threadIdx.x / lanes_per_row;
+  u32x4 o[kDeltaPasses], g[kDeltaPasses];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(bf16_to_f32(o[w] & 0xffffu), bf16_to_f32(g[w] & 0xffffu), acc);
-      acc = fmaf(bf16_to_f32(o[w] >> 16), bf16_to_f32(g[w] >> 16), acc);
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    const long long i = i0 + p * rows_per_pass + r;
+    o[p] = g[p] = u32x4{0, 0, 0, 0};
+    if (i < a.total) {
+      const size_t off = ((size_t)i * a.hq + h) * d + sub * 8;
+      o[p] = *reinterpret_cast<const u32x4*>(a.o + off);
+      g[p] = *reinterpret_cast<const u32x4*>(a.dout + off);
     }
   }
-  for (int off = lanes_per_row / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < nrows && sub == 0) {
-    const long long i = row / a.hq;
-    const int h = (int)(row % a.hq);
-    a.delta[(size_t)h * a.total + i] = acc;
-    a.lse2[(size_t)h * a.total + i] = a.lse[(size_t)h * a.total + i] * kLog2e;
+#pragma unroll
+  for (int p = 0; p < kDeltaPasses; ++p) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(bf16_to_f32(o[p][w] & 0xffffu), bf16_to_f32(g[p][w] & 0xffffu), acc);
+      acc = fmaf(bf16_to_f32(o[p][w] >> 16), bf16_to_f32(g[p][w] >> 16), acc);
+    }
+    for (int off = lanes_per_row / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    const long long i = i0 + p * rows_per_pass + r;
+    if (i < a.total && sub == 0) {
+      a.delta[(size_t)h * a.total + i] = acc;
+      a.lse2[(size_t)h * a.total + i] = a.lse[(size_t)h * a.total + i] * kLog2e;
+    }
   }
 }
 
@@ -877,9 +896,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, int stage, hipStrea
   if (a.nseq <= 0 || a.total <= 0) return hipSuccess;
   // 1. delta
   if (stage == 0 || stage == 1) {
-    const long long nrows = (long long)a.total * a.hq;
-    const int rows_per_wg = 256 / (a.d / 8);
-    const long long nwg = (nrows + rows_per_wg - 1) / rows_per_wg;
+    const int rows_per_wg = 256 / (a.d / 8) * kDeltaPasses;
+    const long long nwg = (long long)((a.total + rows_per_wg - 1) / rows_per_wg) * a.hq;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
