@@ -108,6 +108,19 @@ int main() {
   EXPECT(bca_decode_graph_create(F, F, F, F, FF, 32, 1056, 32, 8, 128, 0.1f, BCA_BF16, 0, F, dneed,
                                  4, nullptr) == BCA_ERR_NULL);
   EXPECT(bca_decode_graph_launch(nullptr, nullptr) == BCA_ERR_NULL);
+  const int32_t* len_dev = reinterpret_cast<const int32_t*>(F);
+  const int32_t* odd = reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(F) + 2);
+  EXPECT(bca_decode_loop_create(F, F, F, F, FF, nullptr, nullptr, 32, 1056, 32, 8, 128, 0.1f,
+                                BCA_BF16, 0, F, dneed, 4, &g) == BCA_ERR_NULL);
+  EXPECT(g == nullptr);
+  EXPECT(bca_decode_loop_create(F, F, F, F, FF, odd, nullptr, 32, 1056, 32, 8, 128, 0.1f,
+                                BCA_BF16, 0, F, dneed, 4, &g) == BCA_ERR_SHAPE);
+  EXPECT(bca_decode_loop_create(F, F, F, F, FF, len_dev, odd, 32, 1056, 32, 8, 128, 0.1f,
+                                BCA_BF16, 0, F, dneed, 4, &g) == BCA_ERR_SHAPE);
+  EXPECT(bca_decode_loop_create(F, F, F, F, FF, len_dev, nullptr, 32, 1056, 32, 8, 128, 0.1f,
+                                BCA_BF16, 0, F, dneed, 0, &g) == BCA_ERR_SHAPE);
+  EXPECT(bca_decode_loop_create(F, F, F, F, FF, len_dev, nullptr, 32, 16, 32, 8, 128, 0.1f,
+                                BCA_BF16, 0, F, dneed, 4, &g) == BCA_ERR_SHAPE);
   bca_decode_graph_destroy(nullptr);
   // packing on random host trajectories, plain and with copy groups
   std::mt19937 rng(12345);
