@@ -135,3 +135,28 @@ def test_loop_runs_the_device_resident_step_count():
             assert torch.isnan(loop.out[n:].float()).all() and torch.isnan(loop.lse[n:]).all()
     finally:
         loop.close()
+
+
+@pytest.mark.parametrize("cap,num_splits", [(96, 1), (64, 0)])
+def test_loop_single_split_with_shorter_cache(cap, num_splits):
+    """One split (no partials, the decode kernel writes O itself) with the
+    device-resident length below the capacity: rows past it are masked."""
+    B, steps = 32, 2
+    w = W.decode_step(cap - B, seed=25)
+    dev = torch.device("cuda", 0)
+    k, v = w.k.to(dev), w.v.to(dev)
+    rng = np.random.default_rng(26)
+    q = torch.from_numpy(rng.standard_normal((steps,) + tuple(w.q.shape), dtype=np.float32))
+    q = q.to(torch.bfloat16).to(dev)
+    kv_len = torch.full((1,), cap, dtype=torch.int32, device=dev)
+    loop = bca.DecodeLoop(q, k, v, kv_len, w.scale, num_splits=num_splits)
+    try:
+        for L in (cap, 40, 33):
+            kv_len.fill_(L)
+            torch.cuda.synchronize()
+            loop.launch()
+            torch.cuda.synchronize()
+            for i in range(steps):
+                _oracle_check(q[i], k[:L], v[:L], w.scale, loop.out[i], loop.lse[i])
+    finally:
+        loop.close()
