@@ -152,6 +152,8 @@ class Probe:
         self.L.bca_probe_read.argtypes = [P, S, I, P, P]
         self.L.bca_probe_mfma.argtypes = [I, I, P, P, P]
         self.L.bca_probe_empty.argtypes = [P]
+        self.L.bca_probe_mfma_lds.argtypes = [I, I, I, P, P, P]
+        self.L.bca_probe_valu.argtypes = [I, I, I, P, P, P]
         self.sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
 
     @staticmethod
@@ -483,11 +485,20 @@ def bench_packing():
 def measured_peaks(probe: Probe, flush):
     """The machine's own peaks: dense bf16 MFMA rate with the clock it ran at,
     streaming read of 1 GiB, a cold read of 34 MB (the P = 8192 decode's
-    bytes) and the event-timed empty kernel."""
+    bytes) and the event-timed empty kernel; then what the attention kernels'
+    ingredients cost: MFMAs with 1 KB of LDS reads per wave for every MFMA
+    (as in the kernels) or every second one, with the clock each ran at, and
+    the issue cycles of v_fma_f32 and v_exp_f32 and of MFMAs with
+    exponentials between them."""
     import torch
     out = torch.zeros(512 * 256, dtype=torch.float32, device="cuda")
-    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    clk = torch.zeros(2 * 512, dtype=torch.int64, device="cuda")
     wgs, iters = 512, 4000
+
+    def clock_mhz() -> float:
+        # median over the workgroups of shader cycles per 100 MHz tick
+        c = clk.cpu().view(-1, 2).double()
+        return float(torch.median(c[:, 0] / c[:, 1].clamp(min=1)) * 100.0)
 
     def mfma():
         rc = probe.L.bca_probe_mfma(iters, wgs, ctypes.c_void_p(out.data_ptr()),
@@ -497,7 +508,7 @@ def measured_peaks(probe: Probe, flush):
 
     per, _ = timed_calls(mfma, 5, 2)
     t_ms = statistics.median(per)
-    cycles, ticks = clk.cpu().tolist()
+    mfma_mhz = clock_mhz()
     tflops = wgs * 4 * iters * 8 * 32768 / (t_ms * 1e-3) / 1e12
     big = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     per, _ = timed_calls(lambda: probe.read(big, 1 << 30, 256), 5, 2)
@@ -506,13 +517,46 @@ def measured_peaks(probe: Probe, flush):
     cold_us = statistics.median(per) * 1e3
     per, _ = timed_calls(probe.empty, 32, 3, flush=flush)
     empty_us = statistics.median(per) * 1e3
+
+    # MFMA with the attention kernels' operand traffic: a 16-byte LDS read
+    # per lane (1 KB per wave) before every MFMA, or before every second one
+    out8 = torch.zeros(512 * 512, dtype=torch.float32, device="cuda")
+    lds = {}
+    for every, label in ((1, "1KB"), (2, "512B")):
+        def run_lds():
+            if probe.L.bca_probe_mfma_lds(1000, 512, every, ctypes.c_void_p(out8.data_ptr()),
+                                          ctypes.c_void_p(clk.data_ptr()), probe.stream()) != 0:
+                raise RuntimeError("probe launch failed")
+        per, _ = timed_calls(run_lds, 5, 2)
+        lds[label] = (512 * 8 * 1000 * 8 * 32768 / (statistics.median(per) * 1e-3) / 1e12,
+                      clock_mhz())
+    # VALU issue cost, cycles per wave-iteration on one SIMD: 16 v_exp_f32
+    # (each after a v_mul_f32), 64 v_fma_f32, 8 MFMAs with the 16 v_exp_f32
+    n_simd = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    valu = {}
+    for kind in (0, 1, 2):
+        def run_valu():
+            if probe.L.bca_probe_valu(kind, 2000, 512, ctypes.c_void_p(out8.data_ptr()),
+                                      ctypes.c_void_p(clk.data_ptr()), probe.stream()) != 0:
+                raise RuntimeError("probe launch failed")
+        per, _ = timed_calls(run_valu, 5, 2)
+        cycles = statistics.median(per) * 1e-3 * clock_mhz() * 1e6
+        valu[kind] = cycles / (512 * 8 * 2000 / n_simd)
+    fma_cyc = valu[1] / 64
     return {"mfma_bf16_TFLOPs": round(tflops, 1),
             "mfma_frac_of_spec": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "clock_MHz_under_mfma": round(cycles / ticks * 100.0, 0),
+            "clock_MHz_under_mfma": round(mfma_mhz, 0),
             "hbm_read_1GiB_GBps": round(read_1g, 1),
             "hbm_read_1GiB_frac_of_spec": round(read_1g / PEAK_HBM_GBS, 4),
             "read_34MB_after_512MB_flush_us_events": round(cold_us, 2),
-            "empty_kernel_after_flush_us_events": round(empty_us, 2)}
+            "empty_kernel_after_flush_us_events": round(empty_us, 2),
+            "mfma_with_1KB_lds_read_each_TFLOPs": round(lds["1KB"][0], 1),
+            "mfma_with_1KB_lds_read_each_clock_MHz": round(lds["1KB"][1], 0),
+            "mfma_with_1KB_lds_read_per_2_TFLOPs": round(lds["512B"][0], 1),
+            "mfma_with_1KB_lds_read_per_2_clock_MHz": round(lds["512B"][1], 0),
+            "v_fma_f32_cycles_per_wave": round(fma_cyc, 2),
+            "v_exp_f32_cycles_per_wave": round((valu[0] - 16 * fma_cyc) / 16, 2),
+            "mfma_plus_exp_cycles_per_8_mfma": round(valu[2], 1)}
 
 
 def cpu_info():
