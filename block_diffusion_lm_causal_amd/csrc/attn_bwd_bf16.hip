@@ -12,17 +12,19 @@
 //
 // Three kernels, no atomics (results are bit-reproducible):
 //   1. delta = rowsum(dO * O) in float32.
-//   2. dK/dV: an 8-wave workgroup owns 128 keys of one KV head.  Waves 0-3
+//   2. dK/dV (bwd_dkdv_kernel, used for head_dim 64; bwd_dkdv_pp_kernel, the
+//      same roles in a two-phase ping-pong over 64-row steps, for head_dim
+//      128): an 8-wave workgroup owns 128 keys of one KV head.  Waves 0-3
 //      ("V waves", 32 keys each) compute S = Q K^T -> P and dV += P^T dO;
 //      waves 4-7 ("K waves", the same keys) compute dP = dO V^T, take P from
 //      their V wave through LDS, form dS and dK += dS^T Q.  S is computed
-//      once, and each SIMD pairs one wave of each kind.  Each wave also
-//      issues its own elementwise work between its MFMAs: a V wave the
+//      once, and each SIMD pairs one wave of each kind.  In bwd_dkdv_kernel
+//      each wave issues its own elementwise work between its MFMAs: a V wave the
 //      exponentials of the next tile between its dV MFMAs, a K wave the dS
 //      of the current tile between the MFMAs of the next tile's dP.  K and V
 //      fragments and the dK/dV accumulators stay in registers; each step
-//      streams a 32-row tile of Q and dO (one query head) through LDS, loaded
-//      straight from HBM three steps ahead.  S is computed with queries on the
+//      streams a 32-row (ping-pong: 64-row) tile of Q and dO of one query head
+//      through LDS, loaded straight from HBM two or three steps ahead.  S is computed with queries on the
 //      M axis, so the P and dS accumulators are, unchanged, the A operands of
 //      the dV and dK products; their B operands (dO and Q with queries on K)
 //      come from the row-major tiles through the transposed LDS read.
@@ -611,6 +613,414 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a, int nkt_max
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dK / dV, ping-pong (head_dim 128): the roles of the kernel above (V
+// waves and K waves of 32 keys each, one of each per SIMD), over 64-row steps
+// and in two phases per step, as the forward's wave groups:
+//   phase 1: V waves  S(t) = Q(t) K^T and dV += P(t-1)^T dO(t-1)   (32 MFMAs)
+//            K waves  dS(t-1) = P(t-1) (dP(t-1) - delta)           (VALU)
+//   phase 2: K waves  dP(t) = dO(t) V^T and dK += dS(t-1)^T Q(t-1) (32 MFMAs)
+//            V waves  P(t) from S(t), handed to the K waves in LDS (VALU)
+// so each SIMD issues MFMAs in both phases, 32 per wave per phase (with
+// 32-row steps a phase held 16, too few to cover the LDS latency at its
+// start).  Tiles t-1 and t are read in step t; tile t+2 is loaded during it,
+// all by the K waves, into the buffer tile t-2 left, and they wait for tile
+// t+1 at the end of the step.
+constexpr int kQt2 = 64;  // query rows per ping-pong step
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_max) {
+  static_assert(D == 128, "ping-pong dK/dV kernel is for head_dim 128");
+  constexpr int kTileBytes = 2 * kQt2 * D * 2;  // Q rows then dO rows
+  constexpr uint32_t kGOff = kQt2 * D * 2;
+  constexpr int kK = D / 16;   // 16-dim chunks
+  constexpr int kDT = D / 32;  // 32-dim tiles of dK / dV
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4][2 * kQt2 * D];
+  __shared__ KvSide lds;
+  // P(t) of V wave h for K wave h: [h][mb][c][lane] (u32x4 = 8 bf16)
+  __shared__ __attribute__((aligned(16))) u32x4 p_xchg[4][2][2][64];
+  const int group = a.hq / a.hkv;
+  const int w = blockIdx.x;
+  const int g = w % a.hkv;
+  const int rest = w / a.hkv;
+  const int ktile = rest % nkt_max;
+  const int seg = rest / nkt_max;
+  const int base = a.cu_seqlens[seg];
+  const int L = a.cu_seqlens[seg + 1] - base;
+  const int k0 = ktile * kKvKeys;
+  if (k0 >= L) return;
+  const Stair stair = make_stair(seg, L, a.block_size, a.s_copies, a.group_start, a.group_pe,
+                                 a.group_copies);
+  const int P = stair.P;
+  const int B = a.block_size;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool kwave = wave >= 4;
+  const int kw0 = k0 + (wave & 3) * 32;
+  const int key = kw0 + (lane & 31);
+  const int k_last_wg = min(k0 + kKvKeys, L) - 1;
+
+  int qs1, qe1, qs2 = 0, qe2 = 0;
+  if (k0 < P) {
+    qs1 = (k0 / B) * B;
+    qe1 = k_last_wg >= P ? min(L, P + ((k_last_wg - P) / B + 1) * B) : P;
+    qs2 = P + first_copy_seeing(stair, k0) * B;
+    qe2 = L;
+    if (qs2 <= qe1) {
+      qe1 = max(qe1, qe2);
+      qs2 = qe2 = 0;
+    }
+  } else {
+    const int c_first = (k0 - P) / B, c_last = (k_last_wg - P) / B;
+    qs1 = P + c_first * B;
+    qe1 = min(L, P + (c_last + 1) * B);
+  }
+  const int nqt1 = (qe1 - qs1 + kQt2 - 1) / kQt2;
+  const int nqt2 = qe2 > qs2 ? (qe2 - qs2 + kQt2 - 1) / kQt2 : 0;
+  const int nsteps = (nqt1 + nqt2) * group;
+
+  // Loads, all by the K waves (load issue in the V waves' phase 2, the longer
+  // one, lengthened the step): a tile is 16 1 KB instructions per tensor, four
+  // per K wave for each of Q and dO; wave 4 also loads the tile's delta rows,
+  // wave 5 its LSE * log2(e) rows.  A K wave issues its Q rows in phase 1 and
+  // its dO rows after its MFMA phase, where it would otherwise wait.
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunks;  // 4
+  constexpr int kDmaPerWave = kQt2 / kRowsPerInst / 4;  // 4
+  const int q_row_elems = a.hq * D;
+  uint32_t dma_voff[kDmaPerWave];
+  int dma_row0[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    dma_row0[j] = ((wave & 3) + 4 * j) * kRowsPerInst;
+    const int R = dma_row0[j] + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz<D>(R);
+    dma_voff[j] = (uint32_t)(R * q_row_elems * 2 + c * 16);
+  }
+  struct Cursor {
+    int t, h;
+  };
+  const int row0_r2 = qs2 + (nqt2 - 1) * kQt2;
+  const int row0_r1 = qs1 + (nqt1 - 1 + nqt2) * kQt2;
+  auto tile_row0 = [&](int t) { return (t < nqt2 ? row0_r2 : row0_r1) - t * kQt2; };
+  auto tile_end = [&](int t) { return t < nqt2 ? qe2 : qe1; };
+  auto advance = [&](Cursor& c) {
+    const int h1 = c.h + 1;
+    const bool wrap = h1 == group;
+    c.h = wrap ? 0 : h1;
+    c.t += wrap ? 1 : 0;
+  };
+  const uint32_t tiles_lds = lds_addr_of(&tiles[0][0]);
+  const bool side_real = wave == 4 || wave == 5;
+  const float* const side_src = wave == 5 ? a.lse2 : a.delta;
+  const uint32_t side_dst = lds_addr_of(&lds.v[0][wave == 5 ? 0 : 1][0]);
+  // Part `part` of this K wave's share of a step's loads (tile of cursor c
+  // into buffer buf): part 0 the Q rows and delta (in phase 1), part 1 the dO
+  // rows and LSE * log2(e) (after the MFMA phase, where the K waves have time
+  // to spare).
+  auto issue_part = [&](const Cursor& c, int buf, bool valid, int part) {
+    const int qt0 = valid ? tile_row0(c.t) : 0;
+    const int head = g * group + c.h;
+    const int rows = valid ? min(tile_end(c.t) - qt0, kQt2) : 0;
+    const uint32_t nbytes = rows > 0 ? (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2) : 0u;
+    const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
+    const uint32_t dst0 = tiles_lds + (uint32_t)(buf * kTileBytes) + (part ? kGOff : 0u);
+    const i32x4 r = rsrc_words((part ? a.dout : a.q) + off, nbytes);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j)
+      buffer_load_lds16_asm(r, dst0 + (uint32_t)(dma_row0[j] * D * 2), dma_voff[j]);
+    if (side_real & ((wave == 4) == (part == 0))) {
+      const size_t so = (size_t)head * a.total + base + qt0;
+      buffer_load_lds4_asm(rsrc_words(side_src + so, (uint32_t)(rows * 4)),
+                           side_dst + (uint32_t)(buf * 2 * 64 * 4), (uint32_t)lane * 4);
+    }
+  };
+  // K waves: wait until only the newest step's loads may be outstanding.
+  auto wait_all_but_newest = [&]() {
+    if (side_real) wait_vmem_le<2 * kDmaPerWave + 1>();
+    else wait_vmem_le<2 * kDmaPerWave>();
+  };
+
+  // K fragments (V waves, B operand of S) or V fragments (K waves, of dP).
+  bf16x8 kvf[kK];
+  {
+    const uint16_t* src = kwave ? a.v : a.k;
+#pragma unroll
+    for (int kk = 0; kk < kK; ++kk) {
+      u32x4 r = u32x4{0, 0, 0, 0};
+      if (key < L) {
+        const size_t off = ((size_t)(base + key) * a.hkv + g) * D + kk * 16 + half * 8;
+        r = *reinterpret_cast<const u32x4*>(src + off);
+      }
+      kvf[kk] = __builtin_bit_cast(bf16x8, r);
+    }
+  }
+  // A fragments of S / dP: Q rows (V waves) or dO rows (K waves); transposed
+  // B fragments of dV / dK: dO (V waves) or Q (K waves).
+  const uint32_t roff0 = row_frag_off<D>(lane, 0) + (kwave ? kGOff : 0u);
+  uint32_t toff[kDT][2];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+    toff[dt][0] = tr_off<D>(lane, dt, 0) + (kwave ? 0u : kGOff);
+    toff[dt][1] = tr_off<D>(lane, dt, 1) + (kwave ? 0u : kGOff);
+  }
+  const char* const tiles_c = reinterpret_cast<const char*>(&tiles[0][0]);
+
+  const int wave_key_last = min(kw0 + 31, L - 1);
+  const bool wave_has_keys = kw0 < L;
+  KeyRows kr = KeyRows{0, 0, 0, 0};
+  if (key < L) kr = key_rows(key, stair);
+  int w1lo = 0, w1hi = 0, w2lo = 0, w2hi = 0, f1lo = 0, f1hi = 0, f2lo = 0, f2hi = 0;
+  if (wave_has_keys) {
+    const KeyRows first = key_rows(kw0, stair), last = key_rows(wave_key_last, stair);
+    if (kw0 < P) {
+      w1lo = first.lo;
+      w1hi = wave_key_last >= P ? max(first.hi, last.hi) : first.hi;
+      w2lo = first.lo2;
+      w2hi = first.hi2;
+    } else {
+      w1lo = first.lo;
+      w1hi = last.hi;
+    }
+    const bool all_clean = wave_key_last < P;
+    const bool one_copy_keys = kw0 >= P && (kw0 - P) / B == (wave_key_last - P) / B;
+    if (kw0 + 31 < L && (all_clean || one_copy_keys)) {
+      f1lo = last.lo;
+      f1hi = last.hi;
+      f2lo = last.lo2;
+      f2hi = last.hi2;
+    }
+  }
+  // Row mask of this lane's key over the 64 rows of tile c: bit 16 mb + r for
+  // row 32 mb + 8 (r/4) + 4 half + r%4 (the rows of accumulator register r
+  // of M block mb); all ones for a tile wholly admitted, zero past the end.
+  auto p_mask = [&](const Cursor& c, bool valid) -> uint32_t {
+    const int qt0 = tile_row0(c.t), qe = tile_end(c.t);
+    const bool act = valid & wave_has_keys &
+                     (((qt0 < w1hi) & (qt0 + kQt2 > w1lo)) | ((qt0 < w2hi) & (qt0 + kQt2 > w2lo)));
+    const bool full = act & (qt0 + kQt2 <= qe) &
+                      (((qt0 >= f1lo) & (qt0 + kQt2 <= f1hi)) |
+                       ((qt0 >= f2lo) & (qt0 + kQt2 <= f2hi)));
+    auto bits = [&](int lo, int hi) -> uint64_t {  // rows [lo, hi) of the tile
+      const int x = min(max(lo - qt0, 0), 64), y = min(max(hi - qt0, 0), 64);
+      const uint64_t hy = y >= 64 ? ~0ull : ((1ull << y) - 1);
+      const uint64_t hx = x >= 64 ? ~0ull : ((1ull << x) - 1);
+      return hy & ~hx;
+    };
+    const uint64_t m = (bits(kr.lo, kr.hi) | bits(kr.lo2, kr.hi2)) & bits(qt0, qe);
+    // rows 32 mb + 8 q + 4 half + e  ->  bit 16 mb + 4 q + e
+    uint32_t out = 0;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint32_t w32 = (uint32_t)(m >> (32 * mb)) >> (4 * half);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out |= ((w32 >> (8 * q)) & 0xfu) << (16 * mb + 4 * q);
+    }
+    return full ? 0xffffffffu : (act ? out : 0u);
+  };
+  auto read_side = [&](int buf, int mb, int r4) {
+    return *reinterpret_cast<const f32x4*>(
+        &lds.v[buf][kwave ? 1 : 0][32 * mb + 8 * r4 + 4 * half]);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  f32x16 acc[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16{};
+
+  // Tiles 0 and 1 before the loop; buffer 3 (the "tile -1" of step 0), its
+  // side values and the P hand-over start as zeros, so step 0's products of
+  // the previous tile add nothing.
+  Cursor ld = Cursor{0, 0};
+  if (kwave) {
+    issue_part(ld, 0, nsteps > 0, 0);
+    issue_part(ld, 0, nsteps > 0, 1);
+    advance(ld);
+    issue_part(ld, 1, nsteps > 1, 0);
+    issue_part(ld, 1, nsteps > 1, 1);
+    advance(ld);
+  }
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&tiles[3][0]);
+    for (int i = tid; i < kTileBytes / 16; i += 512) z[i] = u32x4{0, 0, 0, 0};
+    for (int i = tid; i < 2 * 64; i += 512) lds.v[3][i / 64][i % 64] = 0.f;
+    u32x4* px = &p_xchg[0][0][0][0];
+    for (int i = tid; i < 4 * 2 * 2 * 64; i += 512) px[i] = u32x4{0, 0, 0, 0};
+  }
+  wait_vmem();
+  barrier_lds();
+
+  // MFMA phase of step t (buffers bt = t % 4, bp = (t - 1) % 4): out[mb] =
+  // X(t) Y^T over the 64 rows (X = Q or dO rows, Y = this wave's K or V) and
+  // acc += W(t-1)^T Z(t-1) with W from the words xw (P or dS of tile t-1,
+  // keys on M, rows on K) and Z (dO or Q rows of tile t-1) by transposed
+  // reads.  The two products alternate MFMA by MFMA, with the operands of
+  // each read kAh MFMA pairs ahead.
+  auto mfma_phase = [&](auto cbt, auto cbp, const uint32_t (&xw)[2][2][4], f32x16 (&out)[2]) {
+    constexpr int bt = decltype(cbt)::value, bp = decltype(cbp)::value;
+    uint32_t r0 = roff0;
+    asm volatile("" : "+v"(r0));
+    auto afrag = [&](int i) {  // i = 2 kk + mb
+      const int kk = i >> 1, mb = i & 1;
+      return *reinterpret_cast<const bf16x8*>(tiles_c + bt * kTileBytes + mb * 32 * D * 2 +
+                                              (r0 ^ (32u * kk)));
+    };
+    auto tfrag = [&](int i) {  // i = kDT c + dt, c = 16-row chunk of tile t-1
+      const int c = i / kDT, dt = i % kDT;
+      const char* tb = tiles_c + bp * kTileBytes + c * 16 * D * 2;
+      return tr_pair(tb + toff[dt][0], tb + toff[dt][1]);
+    };
+    constexpr int kN = 2 * kK;  // 16 MFMAs of each product
+    constexpr int kAh = 2;
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 fa[kAh], ft[kAh];
+#pragma unroll
+    for (int i = 0; i < kAh; ++i) {
+      fa[i] = afrag(i);
+      ft[i] = tfrag(i);
+    }
+    out[0] = f32x16{};
+    out[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int c = i / kDT, dt = i % kDT;
+      const bf16x8 xa = __builtin_bit_cast(
+          bf16x8, u32x4{xw[c >> 1][c & 1][0], xw[c >> 1][c & 1][1], xw[c >> 1][c & 1][2],
+                        xw[c >> 1][c & 1][3]});
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, ft[i % kAh], acc[dt], 0, 0, 0);
+      out[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % kAh], kvf[i >> 1], out[i & 1],
+                                                          0, 0, 0);
+      if (i + kAh < kN) {
+        fa[i % kAh] = afrag(i + kAh);
+        ft[i % kAh] = tfrag(i + kAh);
+      }
+    }
+    // issue order: the reads of kAh pairs, then (2 MFMAs, 3 reads) groups,
+    // then the last MFMAs (group masks: 0x100 LDS read, 0x008 MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAh, 0);
+#pragma unroll
+    for (int i = 0; i < kN - kAh; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAh, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (!kwave) {
+    // V waves: phase 1 MFMAs (S(t), dV from P(t-1)); phase 2 P(t).
+    uint32_t pw[2][2][4] = {};  // P(t-1), then P(t): [mb][c][word]
+    u32x4* const pex = &p_xchg[wave & 3][0][0][lane];
+    auto step = [&](int st, auto cbt) {
+      constexpr int bt = decltype(cbt)::value;
+      using BP = std::integral_constant<int, (bt + 3) & 3>;
+      f32x16 s[2];
+      mfma_phase(cbt, BP{}, pw, s);
+      barrier_lds();
+      f32x4 side[2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) side[mb][r4] = read_side(bt, mb, r4);
+      const Cursor cur = Cursor{st / group, st % group};
+      const uint32_t m = p_mask(cur, st < nsteps);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * j + e;
+            const float pv = fast_exp2(fmaf(s[mb][r], a.scale_log2, -side[mb][r >> 2][r & 3]));
+            v[e] = ((m >> (16 * mb + r)) & 1u) ? pv : 0.f;
+          }
+          pw[mb][j >> 2][j & 3] = pack_bf16x2(v[0], v[1]);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          pex[(mb * 2 + c) * 64] = u32x4{pw[mb][c][0], pw[mb][c][1], pw[mb][c][2], pw[mb][c][3]};
+      }
+      barrier_lds();
+    };
+    for (int st = 0; st <= nsteps; st += 4) {
+      step(st, I0{});
+      step(st + 1, I1{});
+      step(st + 2, I2{});
+      step(st + 3, I3{});
+    }
+  } else {
+    // K waves: phase 1 dS(t-1); phase 2 MFMAs (dP(t), dK from dS(t-1)).
+    f32x16 dp[2] = {f32x16{}, f32x16{}};  // dP(t-1), then dP(t)
+    const u32x4* const pex = &p_xchg[wave & 3][0][0][lane];
+    auto step = [&](int st, auto cbt) {
+      constexpr int bt = decltype(cbt)::value;
+      using BP = std::integral_constant<int, (bt + 3) & 3>;
+      issue_part(ld, (bt + 2) & 3, st + 2 < nsteps, 0);
+      uint32_t xw[2][2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x4 side[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) side[r4] = read_side(BP::value, mb, r4);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4 pwc = pex[(mb * 2 + c) * 64];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = pwc[q];
+            const int r = 8 * c + 2 * q;
+            const float v0 = bf16_to_f32(wd & 0xffffu) * (dp[mb][r] - side[r >> 2][r & 3]);
+            const float v1 =
+                bf16_to_f32(wd >> 16) * (dp[mb][r + 1] - side[(r + 1) >> 2][(r + 1) & 3]);
+            xw[mb][c][q] = pack_bf16x2(v0, v1);
+          }
+        }
+      }
+      // dS complete before the barrier (IR passes would sink it into the MFMA phase)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          asm volatile("" ::"v"(xw[mb][c][0]), "v"(xw[mb][c][1]), "v"(xw[mb][c][2]),
+                       "v"(xw[mb][c][3]));
+      barrier_lds();
+      mfma_phase(cbt, BP{}, xw, dp);
+      issue_part(ld, (bt + 2) & 3, st + 2 < nsteps, 1);
+      advance(ld);
+      wait_all_but_newest();
+      barrier_lds();
+    };
+    for (int st = 0; st <= nsteps; st += 4) {
+      step(st, I0{});
+      step(st + 1, I1{});
+      step(st + 2, I2{});
+      step(st + 3, I3{});
+    }
+  }
+
+  if (!wave_has_keys) return;
+  uint16_t* out = kwave ? a.dk : a.dv;
+  const float mul = kwave ? a.scale : 1.f;
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr2 = kw0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (kr2 < L) {
+        const size_t off = ((size_t)(base + kr2) * a.hkv + g) * D + dt * 32 + (lane & 31);
+        out[off] = static_cast<uint16_t>(pack_bf16x2(acc[dt][r] * mul, 0.f) & 0xffffu);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dQ (ping-pong)
 
 template <int D>
@@ -908,7 +1318,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int max_seqlen, int stage, hipStrea
     const long long nkt = (max_seqlen + kKvKeys - 1) / kKvKeys;
     const long long nwg = nkt * a.nseq * a.hkv;
     if (a.d == 128) {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a,
+      hipLaunchKernelGGL(bwd_dkdv_pp_kernel<128>, dim3((unsigned)nwg), dim3(512), 0, stream, a,
                          (int)nkt);
     } else {
       hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)nwg), dim3(512), 0, stream, a,
