@@ -237,12 +237,11 @@ def bench_headline(steps: int, warmup: int):
             c()
             ev[i][j + 1].record()
     torch.cuda.synchronize()
-    names = ["fwd_pp_kernel<128>", "bwd_delta_kernel", "bwd_dkdv_kernel<128>",
+    names = ["fwd_pp_kernel<128>", "bwd_delta_kernel", "bwd_dkdv_pp_kernel<128>",
              "bwd_dq_kernel<128>"]
     kms = {n: statistics.mean(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps))
            for j, n in enumerate(names)}
     return w, pairs, kms, wall_ms, step_ms
-    return w, pairs, kms, wall_ms
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -715,7 +714,7 @@ def main() -> int:
         dkdv_flops = 8.0 * w.d * pairs * w.hq
         value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
         bwd_ms = step_ms["bwd"]
-        achieved = dkdv_flops / (kms["bwd_dkdv_kernel<128>"] * 1e-3) / 1e12
+        achieved = dkdv_flops / (kms["bwd_dkdv_pp_kernel<128>"] * 1e-3) / 1e12
         out.update({
             "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -734,7 +733,7 @@ def main() -> int:
                        "bwd_note": "bwd_ms: the whole backward call; kernel_ms_mean_events: "
                                    "each kernel launched on its own",
                        "kernel_ms_mean_events": {k: round(v, 4) for k, v in kms.items()}},
-            "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel<128>",
+            "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_pp_kernel<128>",
                          "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                          "traffic": stored_traffic("bwd_dkdv_16traj_B64")},
