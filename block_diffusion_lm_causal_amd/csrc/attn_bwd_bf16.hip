@@ -684,8 +684,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
   // Loads, all by the K waves (load issue in the V waves' phase 2, the longer
   // one, lengthened the step): a tile is 16 1 KB instructions per tensor, four
   // per K wave for each of Q and dO; wave 4 also loads the tile's delta rows,
-  // wave 5 its LSE * log2(e) rows.  A K wave issues its Q rows in phase 1 and
-  // its dO rows after its MFMA phase, where it would otherwise wait.
+  // wave 5 its LSE * log2(e) rows.  A K wave issues the side rows and its Q
+  // rows in phase 1 and its dO rows after its MFMA phase, where it would
+  // otherwise wait.
   constexpr int kChunks = D / 8;
   constexpr int kRowsPerInst = 64 / kChunks;  // 4
   constexpr int kDmaPerWave = kQt2 / kRowsPerInst / 4;  // 4
@@ -717,31 +718,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
   const float* const side_src = wave == 5 ? a.lse2 : a.delta;
   const uint32_t side_dst = lds_addr_of(&lds.v[0][wave == 5 ? 0 : 1][0]);
   // Part `part` of this K wave's share of a step's loads (tile of cursor c
-  // into buffer buf): part 0 the Q rows and delta (in phase 1), part 1 the dO
-  // rows and LSE * log2(e) (after the MFMA phase, where the K waves have time
-  // to spare).
+  // into buffer buf): part 0 (in phase 1) the side rows of waves 4 and 5
+  // first, then the Q rows; part 1 the dO rows (after the MFMA phase, where
+  // the K waves have time to spare).
   auto issue_part = [&](const Cursor& c, int buf, bool valid, int part) {
     const int qt0 = valid ? tile_row0(c.t) : 0;
     const int head = g * group + c.h;
     const int rows = valid ? min(tile_end(c.t) - qt0, kQt2) : 0;
     const uint32_t nbytes = rows > 0 ? (uint32_t)((rows - 1) * q_row_elems * 2 + D * 2) : 0u;
     const size_t off = (size_t)(base + qt0) * q_row_elems + (size_t)head * D;
+    if (side_real & (part == 0)) {
+      const size_t so = (size_t)head * a.total + base + qt0;
+      buffer_load_lds4_asm(rsrc_words(side_src + so, (uint32_t)(rows * 4)),
+                           side_dst + (uint32_t)(buf * 2 * 64 * 4), (uint32_t)lane * 4);
+    }
     const uint32_t dst0 = tiles_lds + (uint32_t)(buf * kTileBytes) + (part ? kGOff : 0u);
     const i32x4 r = rsrc_words((part ? a.dout : a.q) + off, nbytes);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j)
       buffer_load_lds16_asm(r, dst0 + (uint32_t)(dma_row0[j] * D * 2), dma_voff[j]);
-    if (side_real & ((wave == 4) == (part == 0))) {
-      const size_t so = (size_t)head * a.total + base + qt0;
-      buffer_load_lds4_asm(rsrc_words(side_src + so, (uint32_t)(rows * 4)),
-                           side_dst + (uint32_t)(buf * 2 * 64 * 4), (uint32_t)lane * 4);
-    }
   };
-  // K waves: wait until only the newest step's loads may be outstanding.
-  auto wait_all_but_newest = [&]() {
-    if (side_real) wait_vmem_le<2 * kDmaPerWave + 1>();
-    else wait_vmem_le<2 * kDmaPerWave>();
-  };
+  // K waves, end of step t: tile t+1 landed.  Only the newest step's Q and
+  // dO rows may still be outstanding; its side rows, issued before them, have
+  // landed too, so tile t+2's LSE rows are readable from step t+1 on.
+  auto wait_all_but_newest = [&]() { wait_vmem_le<2 * kDmaPerWave>(); };
 
   // K fragments (V waves, B operand of S) or V fragments (K waves, of dP).
   bf16x8 kvf[kK];
@@ -820,6 +820,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
     }
     return full ? 0xffffffffu : (act ? out : 0u);
   };
+  // whether tile c is wholly admitted for the wave's 32 keys (wave-uniform)
+  auto p_full = [&](const Cursor& c, bool valid) -> bool {
+    const int qt0 = tile_row0(c.t), qe = tile_end(c.t);
+    return valid & wave_has_keys & (qt0 + kQt2 <= qe) &
+           (((qt0 >= f1lo) & (qt0 + kQt2 <= f1hi)) | ((qt0 >= f2lo) & (qt0 + kQt2 <= f2hi)));
+  };
   auto read_side = [&](int buf, int mb, int r4) {
     return *reinterpret_cast<const f32x4*>(
         &lds.v[buf][kwave ? 1 : 0][32 * mb + 8 * r4 + 4 * half]);
@@ -861,7 +867,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
   // keys on M, rows on K) and Z (dO or Q rows of tile t-1) by transposed
   // reads.  The two products alternate MFMA by MFMA, with the operands of
   // each read kAh MFMA pairs ahead.
-  auto mfma_phase = [&](auto cbt, auto cbp, const uint32_t (&xw)[2][2][4], f32x16 (&out)[2]) {
+  auto mfma_phase = [&](auto cbt, auto cbp, const uint32_t (&xw)[2][2][4], f32x16 (&out)[2],
+                        bool zero_out) {
     constexpr int bt = decltype(cbt)::value, bp = decltype(cbp)::value;
     uint32_t r0 = roff0;
     asm volatile("" : "+v"(r0));
@@ -884,8 +891,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
       fa[i] = afrag(i);
       ft[i] = tfrag(i);
     }
-    out[0] = f32x16{};
-    out[1] = f32x16{};
+    if (zero_out) {
+      out[0] = f32x16{};
+      out[1] = f32x16{};
+    }
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int c = i / kDT, dt = i % kDT;
@@ -913,39 +922,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
   };
 
   if (!kwave) {
-    // V waves: phase 1 MFMAs (S(t), dV from P(t-1)); phase 2 P(t).
+    // V waves: phase 1 MFMAs (S(t), dV from P(t-1)); phase 2 P(t).  The S
+    // accumulators start at -LSE(t) log2(e) / (scale log2(e)) of their rows,
+    // so P = exp2(scale log2(e) S') needs no LDS read in phase 2: tile t+1's
+    // LSE rows are read at the end of step t.
     uint32_t pw[2][2][4] = {};  // P(t-1), then P(t): [mb][c][word]
     u32x4* const pex = &p_xchg[wave & 3][0][0][lane];
-    auto step = [&](int st, auto cbt) {
-      constexpr int bt = decltype(cbt)::value;
-      using BP = std::integral_constant<int, (bt + 3) & 3>;
-      f32x16 s[2];
-      mfma_phase(cbt, BP{}, pw, s);
-      barrier_lds();
-      f32x4 side[2][4];
+    const float neg_inv = -1.f / a.scale_log2;
+    f32x16 s[2];
+    auto load_lse = [&](int buf) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) side[mb][r4] = read_side(bt, mb, r4);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = read_side(buf, mb, r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[mb][4 * r4 + e] = v[e] * neg_inv;
+        }
+    };
+    load_lse(0);
+    auto step = [&](int st, auto cbt) {
+      constexpr int bt = decltype(cbt)::value;
+      using BP = std::integral_constant<int, (bt + 3) & 3>;
+      mfma_phase(cbt, BP{}, pw, s, false);
+      barrier_lds();
       const Cursor cur = Cursor{st / group, st % group};
-      const uint32_t m = p_mask(cur, st < nsteps);
+      // scores outside the admitted pairs to -inf (exp2 gives 0), only on
+      // tiles not wholly admitted
+      if (!p_full(cur, st < nsteps)) {
+        const uint32_t m = p_mask(cur, st < nsteps);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[mb][r] = ((m >> (16 * mb + r)) & 1u) ? s[mb][r] : kNegInf;
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float v[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 2 * j + e;
-            const float pv = fast_exp2(fmaf(s[mb][r], a.scale_log2, -side[mb][r >> 2][r & 3]));
-            v[e] = ((m >> (16 * mb + r)) & 1u) ? pv : 0.f;
-          }
-          pw[mb][j >> 2][j & 3] = pack_bf16x2(v[0], v[1]);
+          const float v0 = fast_exp2(s[mb][2 * j] * a.scale_log2);
+          const float v1 = fast_exp2(s[mb][2 * j + 1] * a.scale_log2);
+          pw[mb][j >> 2][j & 3] = pack_bf16x2(v0, v1);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           pex[(mb * 2 + c) * 64] = u32x4{pw[mb][c][0], pw[mb][c][1], pw[mb][c][2], pw[mb][c][3]};
       }
+      load_lse((bt + 1) & 3);
       barrier_lds();
     };
     for (int st = 0; st <= nsteps; st += 4) {
@@ -990,7 +1013,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
           asm volatile("" ::"v"(xw[mb][c][0]), "v"(xw[mb][c][1]), "v"(xw[mb][c][2]),
                        "v"(xw[mb][c][3]));
       barrier_lds();
-      mfma_phase(cbt, BP{}, xw, dp);
+      mfma_phase(cbt, BP{}, xw, dp, true);
       issue_part(ld, (bt + 2) & 3, st + 2 < nsteps, 1);
       advance(ld);
       wait_all_but_newest();
