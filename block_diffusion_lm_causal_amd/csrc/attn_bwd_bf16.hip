@@ -944,7 +944,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
     auto step = [&](int st, auto cbt) {
       constexpr int bt = decltype(cbt)::value;
       using BP = std::integral_constant<int, (bt + 3) & 3>;
+      // the wave in its MFMA phase gets the higher issue priority, so the
+      // other wave's VALU work fills the gaps between MFMAs instead of
+      // delaying them
+      __builtin_amdgcn_s_setprio(2);
       mfma_phase(cbt, BP{}, pw, s, false);
+      __builtin_amdgcn_s_setprio(0);
       barrier_lds();
       const Cursor cur = Cursor{st / group, st % group};
       // scores outside the admitted pairs to -inf (exp2 gives 0), only on
@@ -1013,7 +1018,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pp_kernel(BwdArgs a, int nkt_
           asm volatile("" ::"v"(xw[mb][c][0]), "v"(xw[mb][c][1]), "v"(xw[mb][c][2]),
                        "v"(xw[mb][c][3]));
       barrier_lds();
+      __builtin_amdgcn_s_setprio(2);  // as the V waves' MFMA phase
       mfma_phase(cbt, BP{}, xw, dp, true);
+      __builtin_amdgcn_s_setprio(0);
       issue_part(ld, (bt + 2) & 3, st + 2 < nsteps, 1);
       advance(ld);
       wait_all_but_newest();
