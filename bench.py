@@ -393,6 +393,43 @@ def bench_decode_calls(prefix: int, flush, calls: int = 16):
             "us_per_call_flushed_median": round(statistics.median(cold) * 1e3, 3)}
 
 
+def bench_decode_splits(flush, calls: int = 32):
+    """Flushed median per decode call for a range of split counts (0 = the
+    library's own plan), bf16 and FP8 caches, P = 1024 and 8192."""
+    import torch
+    from block_diffusion_lm_causal_amd import bca, workloads
+    dev = torch.device("cuda", 0)
+    res = {}
+    for prefix in (1024, 8192):
+        tiles = (prefix + 32 + 63) // 64
+        counts = [0] + [n for n in (1, 2, 3, 4, 6, 8, 9, 13, 17, 22, 26, 32) if n <= tiles]
+        for fp8 in (False, True):
+            if fp8:
+                w, k8, v8, ks, vs = workloads.decode_step_fp8(prefix)
+                q, k, v = w.q.to(dev), k8.to(dev), v8.to(dev)
+            else:
+                w = workloads.decode_step(prefix)
+                q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+            kv_len = prefix + w.block_size
+            o = torch.empty_like(q)
+            lse = torch.empty((w.hq, w.block_size), dtype=torch.float32, device=dev)
+            per = {}
+            for ns in counts:
+                ws = torch.empty(max(bca.decode_workspace(w.block_size, kv_len, w.hq, w.hkv, w.d,
+                                                          ns), 16), dtype=torch.uint8, device=dev)
+                if fp8:
+                    def step():
+                        bca.decode_fp8(q, k, v, ks, vs, w.scale, num_splits=ns, workspace=ws,
+                                       out=o, lse=lse)
+                else:
+                    def step():
+                        bca.decode(q, k, v, w.scale, num_splits=ns, workspace=ws, out=o, lse=lse)
+                cold, _ = timed_calls(step, calls, 3, flush=flush)
+                per["plan" if ns == 0 else str(ns)] = round(statistics.median(cold) * 1e3, 3)
+            res[w.name] = {"us_per_call_flushed_median_by_splits": per}
+    return res
+
+
 def bench_staircase8(steps: int, warmup: int):
     import numpy as np
     import torch
@@ -698,7 +735,7 @@ def main() -> int:
     bca.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda", 0)
     extra = set(p for p in args.paths.split(",") if p)
-    probe = Probe() if extra & {"decode", "decode_calls", "peaks"} else None
+    probe = Probe() if extra & {"decode", "decode_calls", "decode_splits", "peaks"} else None
     flush = flush_read = None
     if probe is not None:
         _flush_buf, flush_read = make_flush(dev, probe)
@@ -753,6 +790,9 @@ def main() -> int:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}, flushed calls only")
             paths[f"decode_P{P}_calls"] = bench_decode_calls(P, flush)
+    if "decode_splits" in extra:  # split-count sweep (not in the default run)
+        log("[bench] decode split-count sweep")
+        paths["decode_splits"] = bench_decode_splits(flush)
     if "decode" in extra:
         for P in (1024, 8192):
             log(f"[bench] decode P={P}")

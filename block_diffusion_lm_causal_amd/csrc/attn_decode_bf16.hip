@@ -19,17 +19,28 @@ namespace {
 // Up to kDecTiles tiles of the chunk are requested from HBM at once, each
 // wave issuing its share tile by tile; tile t becomes readable once every wave
 // has seen its own loads for tiles <= t complete (vmcnt) and passed a barrier,
-// while later tiles are still in flight.  The two groups merge their
-// (max, sum, O) through LDS at the end; the result is the final O and LSE
-// (one chunk) or a float32 partial that the combine kernel merges by
-// log-sum-exp weights.
+// while later tiles are still in flight.  The query rows come the same way
+// (HBM -> LDS, then each wave reads its fragments into registers), and every
+// load is the inline-assembly direct-to-LDS form with plain s_barrier
+// barriers: the compiler then inserts no vmcnt waits of its own.  With the
+// compiler-visible forms it waited for every outstanding load before each
+// tile (a barrier's fence, and a may-alias wait before LDS reads that follow
+// a direct-to-LDS load), so no tile was multiplied before the last had
+// landed.  The two groups merge their (max, sum, O) through LDS at the end;
+// the result is the final O and LSE (one chunk) or a bf16 partial that the
+// combine kernel merges by log-sum-exp weights.
 
 constexpr int kDecTiles = 5;  // key tiles of a chunk staged in LDS at once
 
+// One slot holds a K tile and its V tile; the last slot first holds the
+// workgroup's 128 query rows (the same 2 * 64 * D bf16), which every wave
+// copies to registers before that slot's tile is requested.
 template <int D>
 struct LdsDec {
-  uint16_t k[kDecTiles][kBN * D];
-  uint16_t v[kDecTiles][kBN * D];
+  struct Slot {
+    uint16_t k[kBN * D];
+    uint16_t v[kBN * D];
+  } slot[kDecTiles];
 };
 
 // s_waitcnt vmcnt(N) immediate (vmcnt is split over bits 3:0 and 15:14;
@@ -57,6 +68,7 @@ struct DecWave {
   int split, ntile_all;  // this workgroup's split and its number of key tiles
   int kv_len;            // keys attended (the host's kv_len, or the device-resident length)
   int ntiles_kv;         // 64-key tiles of the whole cache
+  int hg, tok0;          // KV head group, first query token of the workgroup
   int qw0, qi;           // first query row of the wave, the lane's row
   bf16x8 qf[D / 16];     // the lane's query, B operand of S^T = K Q^T
   uint32_t koff[D / 16];     // K fragment offsets in a bf16 tile
@@ -95,17 +107,10 @@ __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& d
   if (a.kv_len_dev) dw.kv_len = min(max(*a.kv_len_dev, a.q_len), a.kv_len);
   dw.ntiles_kv = (dw.kv_len + kBN - 1) / kBN;
   dw.ntile_all = dw.split < dw.ntiles_kv ? (dw.ntiles_kv - dw.split + a.nsplit - 1) / a.nsplit : 0;
+  dw.hg = hg;
+  dw.tok0 = tile * tok;
   dw.qw0 = tile * tok + (dw.wv / a.hpw) * kRows;
   dw.qi = dw.qw0 + (dw.lane & 31);
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 raw = u32x4{0, 0, 0, 0};
-    if (dw.qi < a.q_len) {
-      raw = *reinterpret_cast<const u32x4*>(a.q + ((size_t)dw.qi * a.hq + dw.head) * D +
-                                            kk * 16 + dw.half * 8);
-    }
-    dw.qf[kk] = __builtin_bit_cast(bf16x8, raw);
-  }
   // K rows of this group's key half (32 rows from 32 grp); V rows of that half
   // through the transposed read.
   const int sw = swz<D>(dw.lane & 15);
@@ -123,6 +128,44 @@ __device__ __forceinline__ void dec_wave_init(const DecodeArgs& a, DecWave<D>& d
       dw.voff[dt][sub] = (uint32_t)(row * D * 2 + ((chunk ^ swz<D>(row)) * 16) + (q & 1) * 8);
     }
   }
+}
+
+// This wave's share of the direct-to-LDS loads of the workgroup's query
+// rows into `qlds` (128 rows of D bf16 in the K-tile layout and swizzle):
+// row 32 w + r is token r of the 32-token sub-tile of wave w's head, so
+// every wave w of either group later reads rows 32 (w mod 4) + 0..31.  Rows
+// past q_len lie past the buffer's end and arrive as zeros.
+template <int D>
+__device__ __forceinline__ void dec_issue_q(const DecodeArgs& a, const DecWave<D>& dw,
+                                            uint32_t qlds) {
+  constexpr int kChunks = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunks;
+  constexpr int kInst = 4 * kRows / kRowsPerInst / 8;  // per wave
+  const int tok = kRows * (4 / a.hpw);
+  const int ntok = min(a.q_len - dw.tok0, tok);
+  const i32x4 r = rsrc_words(a.q + (size_t)dw.tok0 * a.hq * D, (uint32_t)(ntok * a.hq * D * 2));
+#pragma unroll
+  for (int j = 0; j < kInst; ++j) {
+    const int row0 = (dw.wave + 8 * j) * kRowsPerInst;
+    const int R = row0 + dw.lane / kChunks;
+    const int w = R / kRows;
+    const int t = (w / a.hpw) * kRows + R % kRows;
+    const int head = dw.hg * a.hpw + w % a.hpw;
+    const uint32_t voff =
+        (uint32_t)(((t * a.hq + head) * D) * 2 + (((dw.lane % kChunks) ^ swz<D>(R)) * 16));
+    buffer_load_lds16_asm(r, qlds + (uint32_t)(row0 * D * 2), voff);
+  }
+}
+
+// The lane's query fragments from the rows dec_issue_q staged (after they
+// have landed for every wave).
+template <int D>
+__device__ __forceinline__ void dec_read_q(const char* qlds, DecWave<D>& dw) {
+  const int sw = swz<D>(dw.lane & 15);
+  const char* row = qlds + (kRows * dw.wv + (dw.lane & 31)) * D * 2;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    dw.qf[kk] = *reinterpret_cast<const bf16x8*>(row + (((2 * kk + dw.half) ^ sw) * 16));
 }
 
 // One 64-key tile for this wave's key half: S^T in two accumulator chains,
@@ -281,28 +324,44 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
   constexpr int kInstPerWaveTile = kInstPerTile / 8;      // 4 (D=128) or 2 (D=64)
   static_assert(kInstPerWaveTile * (kDecTiles - 1) < 64 && kDecTiles <= 6, "vmcnt range");
   DecWave<D> dw;
-  dec_wave_init<D>(a, dw);  // query fragments first: every later vmcnt wait covers them
+  dec_wave_init<D>(a, dw);
   const int kv_elems = a.hkv * D;
   const uint16_t* kb = a.k + (size_t)dw.kv_head * D;
   const uint16_t* vb = a.v + (size_t)dw.kv_head * D;
+  const uint32_t slots = lds_addr_of(&lds.slot[0]);
+  constexpr uint32_t kSlotBytes = sizeof(typename LdsDec<D>::Slot);
 
-  // This wave's loads of one tile: instructions wave + 8 j of the tile's
-  // kInstPerTile (K blocks, then V blocks).
-  auto load_tile = [&](int t_round, int i) {
+  // This wave's loads of one tile into slot `sl`: instructions wave + 8 j of
+  // the tile's kInstPerTile (K blocks, then V blocks).
+  auto load_tile = [&](int sl, int i) {
     const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
     const int rows = min(dw.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * kv_elems * 2 + D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * kv_elems, nbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * kv_elems, nbytes);
+    const i32x4 rk = rsrc_words(kb + (size_t)k0 * kv_elems, nbytes);
+    const i32x4 rv = rsrc_words(vb + (size_t)k0 * kv_elems, nbytes);
 #pragma unroll
     for (int j = 0; j < kInstPerWaveTile; ++j) {
-      const int i = dw.wave + 8 * j;
-      const bool is_k = i < kInstPerTile / 2;
-      const int row0 = (is_k ? i : i - kInstPerTile / 2) * kRowsPerInst;
+      const int ii = dw.wave + 8 * j;
+      const bool is_k = ii < kInstPerTile / 2;
+      const int row0 = (is_k ? ii : ii - kInstPerTile / 2) * kRowsPerInst;
       const int R = row0 + dw.lane / kChunks;
       const uint32_t voff = (uint32_t)(R * kv_elems * 2 + (((dw.lane % kChunks) ^ swz<D>(R)) * 16));
-      if (is_k) buffer_load_lds16(rk, lds.k[t_round] + row0 * D, voff);
-      else buffer_load_lds16(rv, lds.v[t_round] + row0 * D, voff);
+      const uint32_t dst = slots + (uint32_t)sl * kSlotBytes + (is_k ? 0u : (uint32_t)(kBN * D * 2)) +
+                           (uint32_t)(row0 * D * 2);
+      buffer_load_lds16_asm(is_k ? rk : rv, dst, voff);
+    }
+  };
+  // Tiles t = 0 .. nt-1 of a round, in slots 0 .. nt-1, all requested: tile t
+  // has landed for this wave once at most the loads of the later tiles are
+  // outstanding, and for every wave after the barrier.
+  auto consume = [&](int r0, int nt, WaveState<D>& ws) {
+    for (int t = 0; t < nt; ++t) {
+      wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
+      barrier_lds();
+      dec_tile<D>(reinterpret_cast<const char*>(lds.slot[t].k),
+                  reinterpret_cast<const char*>(lds.slot[t].v), dw,
+                  split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, dw.kv_len,
+                  a.scale_log2, ws);
     }
   };
 
@@ -311,21 +370,27 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_bf16_kernel(DecodeArgs a
   for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
   ws.m = kNegBig;
   ws.l = 0.f;
-  for (int r0 = 0; r0 < dw.ntile_all; r0 += kDecTiles) {
-    const int nt = min(kDecTiles, dw.ntile_all - r0);
-    if (r0 > 0) __syncthreads();  // the previous round's tiles have been consumed
-    for (int t = 0; t < nt; ++t) load_tile(t, r0 + t);
-    for (int t = 0; t < nt; ++t) {
-      // tile t has landed once at most the loads of tiles t+1.. are outstanding
-      wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
-      __syncthreads();
-      dec_tile<D>(reinterpret_cast<const char*>(lds.k[t]), reinterpret_cast<const char*>(lds.v[t]),
-                  dw, split_tile(dw.split, a.nsplit, r0 + t) * kBN + 32 * dw.grp, dw.kv_len,
-                  a.scale_log2, ws);
-    }
+  // Round 0: the query rows into the last slot, then tiles 0 .. nt0-1; once
+  // the query rows have landed and every wave holds its fragments, the last
+  // slot takes tile kDecTiles-1.
+  const int nt = min(kDecTiles, dw.ntile_all);
+  const int nt0 = min(kDecTiles - 1, dw.ntile_all);
+  dec_issue_q<D>(a, dw, slots + (uint32_t)(kDecTiles - 1) * kSlotBytes);
+  for (int t = 0; t < nt0; ++t) load_tile(t, t);
+  wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * nt0);
+  barrier_lds();
+  dec_read_q<D>(reinterpret_cast<const char*>(&lds.slot[kDecTiles - 1]), dw);
+  barrier_lds();  // every wave's query reads are done: the slot is free
+  if (nt > nt0) load_tile(kDecTiles - 1, kDecTiles - 1);
+  consume(0, nt, ws);
+  for (int r0 = kDecTiles; r0 < dw.ntile_all; r0 += kDecTiles) {
+    const int ntr = min(kDecTiles, dw.ntile_all - r0);
+    barrier_lds();  // the previous round's tiles have been consumed
+    for (int t = 0; t < ntr; ++t) load_tile(t, r0 + t);
+    consume(r0, ntr, ws);
   }
   __syncthreads();  // the tile buffers are free for the merge
-  dec_finish<D>(a, dw, reinterpret_cast<float*>(&lds.k[0][0]), ws);
+  dec_finish<D>(a, dw, reinterpret_cast<float*>(&lds.slot[0]), ws);
 }
 
 // FP8 K/V cache (OCP E4M3; the pages run their decode with an FP8 KV cache,
@@ -342,6 +407,7 @@ template <int D>
 struct LdsDec8 {
   uint8_t k8[kDec8Tiles][kBN * D];
   uint8_t v8[kDec8Tiles][kBN * D];
+  uint16_t q[4 * kRows * D];  // the workgroup's query rows (dec_issue_q)
 };
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -376,6 +442,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   static_assert(kInstPerWaveTile * (kDec8Tiles - 1) < 64 && kDec8Tiles <= 6, "vmcnt range");
   DecWave<D> dw;
   dec_wave_init<D>(a, dw);
+  dec_issue_q<D>(a, dw, lds_addr_of(&lds.q[0]));
   const int row_bytes = a.hkv * D;
   const uint8_t* kb = a.k8 + (size_t)dw.kv_head * D;
   const uint8_t* vb = a.v8 + (size_t)dw.kv_head * D;
@@ -414,12 +481,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   // kInstPerTile (K blocks, then V blocks); lane l of an instruction fills
   // physical chunk l % kChunks8 of its row with the logical chunk the
   // swizzle puts there.
+  const uint32_t k8_lds = lds_addr_of(&lds.k8[0][0]);
+  const uint32_t v8_lds = lds_addr_of(&lds.v8[0][0]);
   auto load_tile = [&](int t_round, int i) {
     const int k0 = split_tile(dw.split, a.nsplit, i) * kBN;
     const int rows = min(dw.kv_len - k0, kBN);
     const uint32_t nbytes = (uint32_t)((rows - 1) * row_bytes + D);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (size_t)k0 * row_bytes, nbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (size_t)k0 * row_bytes, nbytes);
+    const i32x4 rk = rsrc_words(kb + (size_t)k0 * row_bytes, nbytes);
+    const i32x4 rv = rsrc_words(vb + (size_t)k0 * row_bytes, nbytes);
 #pragma unroll
     for (int j = 0; j < kInstPerWaveTile; ++j) {
       const int ii = dw.wave + 8 * j;
@@ -427,8 +496,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
       const int row0 = (is_k ? ii : ii - kInstPerTile / 2) * kRowsPerInst;
       const int R = row0 + lane / kChunks8;
       const uint32_t voff = (uint32_t)(R * row_bytes + (((lane % kChunks8) ^ swz8<D>(R)) * 16));
-      if (is_k) buffer_load_lds16(rk, lds.k8[t_round] + row0 * D, voff);
-      else buffer_load_lds16(rv, lds.v8[t_round] + row0 * D, voff);
+      const uint32_t dst = (is_k ? k8_lds : v8_lds) + (uint32_t)(t_round * kBN * D + row0 * D);
+      buffer_load_lds16_asm(is_k ? rk : rv, dst, voff);
     }
   };
 
@@ -437,13 +506,26 @@ __global__ __launch_bounds__(kPPThreads, 1) void decode_fp8_kernel(DecodeArgs a)
   for (int dt = 0; dt < D / 32; ++dt) ws.acc[dt] = f32x16{};
   ws.m = kNegBig;
   ws.l = 0.f;
+  // The query rows were requested first: once at most the first round's
+  // tile loads are outstanding they have landed for this wave, and for every
+  // wave after the barrier.  (All loads here are the inline-assembly form, so
+  // the compiler adds no vmcnt waits of its own; see the bf16 kernel.)
+  {
+    const int nt = min(kDec8Tiles, dw.ntile_all);
+    for (int t = 0; t < nt; ++t) load_tile(t, t);
+    wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * nt);
+    barrier_lds();
+    dec_read_q<D>(reinterpret_cast<const char*>(&lds.q[0]), dw);
+  }
   for (int r0 = 0; r0 < dw.ntile_all; r0 += kDec8Tiles) {
     const int nt = min(kDec8Tiles, dw.ntile_all - r0);
-    if (r0 > 0) __syncthreads();  // the previous round's tiles have been consumed
-    for (int t = 0; t < nt; ++t) load_tile(t, r0 + t);
+    if (r0 > 0) {
+      barrier_lds();  // the previous round's tiles have been consumed
+      for (int t = 0; t < nt; ++t) load_tile(t, r0 + t);
+    }
     for (int t = 0; t < nt; ++t) {
       wait_vmem_upto<kInstPerWaveTile>(kInstPerWaveTile * (nt - 1 - t));
-      __syncthreads();  // tile t has landed for every wave
+      barrier_lds();  // tile t has landed for every wave
       const char* kt = reinterpret_cast<const char*>(lds.k8[t]);
       const char* vt = reinterpret_cast<const char*>(lds.v8[t]);
       auto kfrag = [&](int kk) {
