@@ -40,6 +40,9 @@ SMALL = [
     ("no_groups_segment", [[(0, 2), (32, 1)], [], [(32, 2)]], [2, 3, 2], 4, 2, 128, 32),
     ("pe_zero_only", [[(0, 5)]], [3], 4, 2, 128, 32),
     ("B8_odd_tiles", [[(0, 3), (8, 2), (24, 4), (40, 1)]], [7], 8, 8, 128, 8),
+    # long group tables: 64 and 65 groups in one segment (one per block)
+    ("groups_64_one_segment", [[(4 * b, 1 + b % 2) for b in range(64)]], [64], 4, 2, 64, 4),
+    ("groups_65_one_segment", [[(4 * b, 1 + (b % 3 == 0)) for b in range(65)]], [65], 4, 2, 64, 4),
 ]
 
 
