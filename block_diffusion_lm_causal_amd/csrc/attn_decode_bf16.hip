@@ -254,12 +254,18 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
                                            WaveState<D>& ws) {
   const int lane = dw.lane;
   constexpr int kWaveFloats = (D / 32) * 16 * 64 + 128;
+  // 16 bytes per lane and instruction: element (dt, r) of lane l at
+  // float 4 ((dt * 4 + r / 4) * 64 + l) + r % 4 of the wave's area.
   if (dw.grp == 1) {
     float* dst = mrg + dw.wv * kWaveFloats;
+    f32x4* dst4 = reinterpret_cast<f32x4*>(dst);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(dt * 16 + r) * 64 + lane] = ws.acc[dt][r];
+      for (int r4 = 0; r4 < 4; ++r4)
+        dst4[(dt * 4 + r4) * 64 + lane] =
+            f32x4{ws.acc[dt][4 * r4], ws.acc[dt][4 * r4 + 1], ws.acc[dt][4 * r4 + 2],
+                  ws.acc[dt][4 * r4 + 3]};
     }
     dst[(D / 32) * 16 * 64 + lane] = ws.m;
     dst[(D / 32) * 16 * 64 + 64 + lane] = ws.l;
@@ -268,6 +274,7 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
   if (dw.grp == 1) return;
   {
     const float* src = mrg + dw.wv * kWaveFloats;
+    const f32x4* src4 = reinterpret_cast<const f32x4*>(src);
     const float mb = src[(D / 32) * 16 * 64 + lane];
     const float lb = src[(D / 32) * 16 * 64 + 64 + lane];
     const float m_new = fmaxf(ws.m, mb);
@@ -275,8 +282,14 @@ __device__ __forceinline__ void dec_finish(const DecodeArgs& a, const DecWave<D>
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ws.acc[dt][r] = (ws.acc[dt][r] * sa + src[(dt * 16 + r) * 64 + lane] * sb) * a.o_mul;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 b = src4[(dt * 4 + r4) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          ws.acc[dt][r] = (ws.acc[dt][r] * sa + b[e] * sb) * a.o_mul;
+        }
+      }
     }
     ws.l = ws.l * sa + lb * sb;
     ws.m = m_new;
