@@ -46,6 +46,17 @@ def test_fp8_decode_edge_shapes(P, B, hq, hkv, d):
     assert max_abs(o, O) <= TOL_BF16 and max_abs(lse, LSE) <= TOL_BF16
 
 
+# Rounds of up to five key tiles per workgroup: 5 + 1 and 5 + 2 (129 tiles in
+# 21 splits), 5 + 5 and 5 + 5 + 1 (32 tiles in 3 splits), against the oracle.
+@pytest.mark.parametrize("P,ns", [(8192, 21), (2048 - 32, 3)])
+def test_fp8_multi_round_splits_match_oracle(P, ns):
+    w, k8, v8, ks, vs, o, lse = run(P, num_splits=ns)
+    K = oracle.e4m3_to_float(k8.numpy()) * ks
+    V = oracle.e4m3_to_float(v8.numpy()) * vs
+    O, LSE = oracle.decode(w.q, K, V, w.scale)
+    assert max_abs(o, O) <= TOL_BF16 and max_abs(lse, LSE) <= TOL_BF16
+
+
 def test_fp8_split_invariance_and_determinism():
     ref = run(4096, num_splits=1)
     for ns in (3, 16, 0):

@@ -42,6 +42,19 @@ def test_decode_edge_shapes(P, B, hq, hkv, d):
     assert max_abs(o, O) <= TOL_BF16 and max_abs(lse, LSE) <= TOL_BF16
 
 
+# A workgroup takes the key tiles of its split in rounds of up to five (the
+# first round's fifth tile after the query rows): splits of 5 + 1 and 5 + 2
+# tiles (129 tiles in 21 splits), 5 + 5 and 5 + 5 + 1 (32 tiles in 3 splits)
+# and four rounds (513 tiles in 31 splits, the library's plan), each against
+# the oracle.
+@pytest.mark.parametrize("P,ns", [(8192, 21), (2048 - 32, 3), (32768, 0)])
+def test_decode_multi_round_splits_match_oracle(P, ns):
+    w = W.decode_step(P)
+    o, lse = run_decode(w, num_splits=ns)
+    O, LSE = oracle.decode(w.q, w.k, w.v, w.scale)
+    assert max_abs(o, O) <= TOL_BF16 and max_abs(lse, LSE) <= TOL_BF16
+
+
 def test_split_count_invariance():
     w = W.decode_step(8192)
     ref_o, ref_l = run_decode(w, num_splits=1)
