@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "../../include/bca.h"
@@ -84,9 +85,10 @@ hipError_t to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
 //   with copies, P % B = 0; copy groups: group_start non-decreasing from 0,
 //   each pe a multiple of B in [0, P], non-decreasing within the segment,
 //   copies >= 0.
-bca_status_t validate_tables(const int32_t* cu, const int32_t* s_copies, const int32_t* gstart,
-                             const int32_t* gpe, const int32_t* gcp, int32_t nseq,
-                             int32_t max_seqlen, int32_t total, int32_t B, hipStream_t s) {
+bca_status_t validate_tables_impl(const int32_t* cu, const int32_t* s_copies,
+                                  const int32_t* gstart, const int32_t* gpe, const int32_t* gcp,
+                                  int32_t nseq, int32_t max_seqlen, int32_t total, int32_t B,
+                                  hipStream_t s) {
   std::vector<int32_t> hcu, hsc, hgs, hpe, hcp;
   hipError_t err = to_host(hcu, cu, (size_t)nseq + 1, s);
   if (err == hipSuccess && s_copies) err = to_host(hsc, s_copies, (size_t)nseq, s);
@@ -150,6 +152,19 @@ bca_status_t validate_tables(const int32_t* cu, const int32_t* s_copies, const i
   return BCA_OK;
 }
 
+// No exception crosses the C ABI: a failed host allocation of the copies
+// becomes a status.
+bca_status_t validate_tables(const int32_t* cu, const int32_t* s_copies, const int32_t* gstart,
+                             const int32_t* gpe, const int32_t* gcp, int32_t nseq,
+                             int32_t max_seqlen, int32_t total, int32_t B, hipStream_t s) {
+  try {
+    return validate_tables_impl(cu, s_copies, gstart, gpe, gcp, nseq, max_seqlen, total, B, s);
+  } catch (const std::bad_alloc&) {
+    return fail(BCA_ERR_HOST_MEMORY, "validation: no host memory for copies of %d segments",
+                nseq);
+  }
+}
+
 bca_status_t poison(void* p, size_t bytes, hipStream_t s) {
   return hip_status(bca::launch_fill_u32(p, bytes / 4, kPoisonWord, s), "poison fill");
 }
@@ -169,6 +184,7 @@ const char* bca_status_string(bca_status_t status) {
     case BCA_ERR_UNSUPPORTED: return "unsupported configuration";
     case BCA_ERR_WORKSPACE: return "workspace too small";
     case BCA_ERR_HIP: return "HIP runtime error";
+    case BCA_ERR_HOST_MEMORY: return "host memory exhausted";
     default: return "unknown status";
   }
 }
@@ -591,7 +607,12 @@ static bca_status_t capture_decode(const bca::DecodeArgs& a0, int32_t steps, siz
     (void)hipGraphDestroy(g);
     return hip_status(err, "graph instantiate");
   }
-  *graph = new bca_decode_graph{g, exec, steps};
+  *graph = new (std::nothrow) bca_decode_graph{g, exec, steps};
+  if (!*graph) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(g);
+    return fail(BCA_ERR_HOST_MEMORY, "no host memory for the graph handle");
+  }
   return BCA_OK;
 }
 

@@ -21,6 +21,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <algorithm>
+#include <new>
 #include <numeric>
 #include <vector>
 
@@ -103,18 +104,17 @@ void lpt_assign(const std::vector<int64_t>& cost, int32_t nbins, int32_t* bin_of
   for (int32_t t : by_cost) order[fill[bin_of[t]]++] = t;
 }
 
-}  // namespace
-
-extern "C" {
-
-bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, int32_t ntraj,
-                               int32_t block_size, int32_t nbins, int32_t* bin_of,
-                               int64_t* bin_cost, int32_t* order, int32_t* bin_start) {
+// The packing entry points' bodies (their wrappers turn a failed host
+// allocation into a status: no exception crosses the C ABI).
+bca_status_t pack_balanced_impl(const int32_t* seqlens, const int32_t* s_copies, int32_t ntraj,
+                                int32_t block_size, int32_t nbins, int32_t* bin_of,
+                                int64_t* bin_cost, int32_t* order, int32_t* bin_start) {
   g_pack_error[0] = '\0';
   if (ntraj < 0 || nbins < 1 || block_size < 1)
     return pack_fail(BCA_ERR_SHAPE, "need ntraj >= 0 (%lld), nbins >= 1 (%lld), block_size >= 1",
                      ntraj, nbins);
-  if (ntraj > 0 && (!seqlens || !bin_of || !order)) return pack_fail(BCA_ERR_NULL, "a required pointer is NULL", 0, 0);
+  if (ntraj > 0 && (!seqlens || !bin_of || !order))
+    return pack_fail(BCA_ERR_NULL, "a required pointer is NULL", 0, 0);
   if (!bin_cost || !bin_start) return pack_fail(BCA_ERR_NULL, "a required pointer is NULL", 0, 0);
   std::vector<int64_t> cost(ntraj);
   for (int32_t t = 0; t < ntraj; ++t) {
@@ -128,11 +128,11 @@ bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, 
   return BCA_OK;
 }
 
-bca_status_t bca_pack_balanced_groups(const int32_t* seqlens, const int32_t* group_start,
-                                      const int32_t* group_pe, const int32_t* group_copies,
-                                      int32_t ntraj, int32_t block_size, int32_t nbins,
-                                      int32_t* bin_of, int64_t* bin_cost, int32_t* order,
-                                      int32_t* bin_start) {
+bca_status_t pack_balanced_groups_impl(const int32_t* seqlens, const int32_t* group_start,
+                                       const int32_t* group_pe, const int32_t* group_copies,
+                                       int32_t ntraj, int32_t block_size, int32_t nbins,
+                                       int32_t* bin_of, int64_t* bin_cost, int32_t* order,
+                                       int32_t* bin_start) {
   g_pack_error[0] = '\0';
   if (ntraj < 0 || nbins < 1 || block_size < 1)
     return pack_fail(BCA_ERR_SHAPE, "need ntraj >= 0 (%lld), nbins >= 1 (%lld), block_size >= 1",
@@ -157,6 +157,36 @@ bca_status_t bca_pack_balanced_groups(const int32_t* seqlens, const int32_t* gro
   }
   lpt_assign(cost, nbins, bin_of, bin_cost, order, bin_start);
   return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bca_status_t bca_pack_balanced(const int32_t* seqlens, const int32_t* s_copies, int32_t ntraj,
+                               int32_t block_size, int32_t nbins, int32_t* bin_of,
+                               int64_t* bin_cost, int32_t* order, int32_t* bin_start) {
+  try {
+    return pack_balanced_impl(seqlens, s_copies, ntraj, block_size, nbins, bin_of, bin_cost,
+                              order, bin_start);
+  } catch (const std::bad_alloc&) {
+    return pack_fail(BCA_ERR_HOST_MEMORY, "no host memory for %lld trajectories in %lld bins",
+                     ntraj, nbins);
+  }
+}
+
+bca_status_t bca_pack_balanced_groups(const int32_t* seqlens, const int32_t* group_start,
+                                      const int32_t* group_pe, const int32_t* group_copies,
+                                      int32_t ntraj, int32_t block_size, int32_t nbins,
+                                      int32_t* bin_of, int64_t* bin_cost, int32_t* order,
+                                      int32_t* bin_start) {
+  try {
+    return pack_balanced_groups_impl(seqlens, group_start, group_pe, group_copies, ntraj,
+                                     block_size, nbins, bin_of, bin_cost, order, bin_start);
+  } catch (const std::bad_alloc&) {
+    return pack_fail(BCA_ERR_HOST_MEMORY, "no host memory for %lld trajectories in %lld bins",
+                     ntraj, nbins);
+  }
 }
 
 const char* bca_pack_last_error(void) { return g_pack_error; }

@@ -87,7 +87,10 @@ typedef enum {
   BCA_ERR_DTYPE = 3,       /* element type not supported by this entry point */
   BCA_ERR_UNSUPPORTED = 4, /* head_dim or head grouping not implemented */
   BCA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-  BCA_ERR_HIP = 6          /* the HIP runtime refused a launch */
+  BCA_ERR_HIP = 6,         /* the HIP runtime refused a launch */
+  BCA_ERR_HOST_MEMORY = 7  /* host memory for the library's own small host-side
+                              arrays (validation copies, packing, graph handles)
+                              could not be allocated; nothing was enqueued */
 } bca_status_t;
 
 typedef enum { BCA_F32 = 0, BCA_BF16 = 1 } bca_dtype_t;

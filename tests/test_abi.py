@@ -203,8 +203,10 @@ def test_backward_stage_checks(L):
 
 
 def test_status_strings_cover_every_code(L):
-    names = {L.bca_status_string(c) for c in range(7)}
-    assert len(names) == 7 and b"unknown status" not in names
+    names = {L.bca_status_string(c) for c in range(8)}
+    assert len(names) == 8 and b"unknown status" not in names
+    assert L.bca_status_string(7) == b"host memory exhausted"
+    assert L.bca_status_string(8) == b"unknown status"
 
 
 def test_noalloc_decode_checks_before_touching_the_gpu(L):
