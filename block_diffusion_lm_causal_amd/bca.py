@@ -135,6 +135,14 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on(device: torch.device, fn, *args):
+    """Call a library entry point with the tensors' device current (the C ABI
+    takes the calling thread's current device to be the device of its
+    pointers and stream, as HIP does)."""
+    with torch.cuda.device(device):
+        return fn(*args)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return BCA_BF16
@@ -215,9 +223,10 @@ def staircase_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
-    st = lib().bca_staircase_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                 _ptr(cu_seqlens), _ptr(s_copies), nseq, max_seqlen, total, hq,
-                                 hkv, d, int(block_size), scale, _dtype_code(q), _stream(dev))
+    st = _on(dev, lib().bca_staircase_fwd,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), _ptr(s_copies),
+             nseq, max_seqlen, total, hq, hkv, d, int(block_size), scale, _dtype_code(q),
+             _stream(dev))
     _check("bca_staircase_fwd", st)
     return out, lse
 
@@ -237,9 +246,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Ten
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
-    st = lib().bca_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), nseq,
-                       max_seqlen, total, hq, hkv, d, int(block_size), scale, _dtype_code(q),
-                       _stream(dev))
+    st = _on(dev, lib().bca_fwd,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), nseq, max_seqlen,
+             total, hq, hkv, d, int(block_size), scale, _dtype_code(q), _stream(dev))
     _check("bca_fwd", st)
     return out, lse
 
@@ -274,10 +283,10 @@ def staircase_groups_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, total), dtype=torch.float32, device=dev)
-    st = lib().bca_staircase_groups_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                        _ptr(cu_seqlens), _ptr(group_start), _ptr(group_pe),
-                                        _ptr(group_copies), nseq, max_seqlen, total, hq, hkv, d,
-                                        int(block_size), scale, _dtype_code(q), _stream(dev))
+    st = _on(dev, lib().bca_staircase_groups_fwd,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), _ptr(group_start),
+             _ptr(group_pe), _ptr(group_copies), nseq, max_seqlen, total, hq, hkv, d,
+             int(block_size), scale, _dtype_code(q), _stream(dev))
     _check("bca_staircase_groups_fwd", st)
     return out, lse
 
@@ -318,13 +327,11 @@ def staircase_groups_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: t
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib().bca_staircase_groups_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                                        _ptr(cu_seqlens), _ptr(group_start), _ptr(group_pe),
-                                        _ptr(group_copies), nseq, max_seqlen, total, hq, hkv, d,
-                                        int(block_size), scale, _dtype_code(q), _ptr(workspace),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream(dev))
+    st = _on(dev, lib().bca_staircase_groups_bwd,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+             _ptr(dv), _ptr(cu_seqlens), _ptr(group_start), _ptr(group_pe), _ptr(group_copies),
+             nseq, max_seqlen, total, hq, hkv, d, int(block_size), scale, _dtype_code(q),
+             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check("bca_staircase_groups_bwd", st)
     return dq, dk, dv
 
@@ -357,12 +364,11 @@ def staircase_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib().bca_staircase_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                                       _ptr(cu_seqlens), _ptr(s_copies), nseq, max_seqlen, total,
-                                       hq, hkv, d, int(block_size), scale, _dtype_code(q),
-                                       _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(dev))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _on(dev, lib().bca_staircase_bwd_stage,
+             int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+             _ptr(dk), _ptr(dv), _ptr(cu_seqlens), _ptr(s_copies), nseq, max_seqlen, total, hq, hkv,
+             d, int(block_size), scale, _dtype_code(q), _ptr(workspace), ws_bytes, _stream(dev))
     _check("bca_staircase_bwd_stage", st)
     return dq, dk, dv
 
@@ -412,9 +418,9 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
-    st = lib().bca_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv,
-                          d, scale, _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
-                          _stream(dev))
+    st = _on(dev, lib().bca_decode,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv, d, scale,
+             _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes, _stream(dev))
     _check("bca_decode", st)
     return out, lse
 
@@ -434,9 +440,9 @@ def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
-    st = lib().bca_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len,
-                                  hq, hkv, d, scale, _dtype_code(q), int(num_splits),
-                                  _stream(dev))
+    st = _on(dev, lib().bca_decode_noalloc,
+             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv, d, scale,
+             _dtype_code(q), int(num_splits), _stream(dev))
     _check("bca_decode_noalloc", st)
     return out, lse
 
@@ -461,9 +467,10 @@ def decode_fp8(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: flo
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((hq, q_len), dtype=torch.float32, device=dev)
-    st = lib().bca_decode_fp8(_ptr(q), _ptr(k8), _ptr(v8), float(k_scale), float(v_scale),
-                              _ptr(out), _ptr(lse), q_len, kv_len, hq, hkv, d, scale,
-                              int(num_splits), _ptr(workspace), ws_bytes, _stream(dev))
+    st = _on(dev, lib().bca_decode_fp8,
+             _ptr(q), _ptr(k8), _ptr(v8), float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
+             q_len, kv_len, hq, hkv, d, scale, int(num_splits), _ptr(workspace), ws_bytes,
+             _stream(dev))
     _check("bca_decode_fp8", st)
     return out, lse
 
@@ -493,23 +500,24 @@ class DecodeGraph:
         self._keep = (q, k, v, workspace)
         self._dev = dev
         self._handle = _P()
-        st = lib().bca_decode_graph_create(_ptr(q), _ptr(k), _ptr(v), _ptr(self.out),
-                                           _ptr(self.lse), q_len, kv_len, hq, hkv, d, scale,
-                                           _dtype_code(q), int(num_splits), _ptr(workspace),
-                                           ws_bytes, int(steps), ctypes.byref(self._handle))
+        st = _on(dev, lib().bca_decode_graph_create,
+                 _ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), q_len, kv_len, hq, hkv,
+                 d, scale, _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes, int(steps),
+                 ctypes.byref(self._handle))
         _check("bca_decode_graph_create", st)
         self.steps = int(steps)
 
     def launch(self) -> None:
         """Enqueue one replay (all steps) on torch's current stream."""
         _check("bca_decode_graph_launch",
-               lib().bca_decode_graph_launch(self._handle, _stream(self._dev)))
+               _on(self._dev, lib().bca_decode_graph_launch, self._handle,
+                   _stream(self._dev)))
 
     def close(self) -> None:
         """Release the graph after synchronising its device."""
         if self._handle:
             torch.cuda.synchronize(self._dev)
-            lib().bca_decode_graph_destroy(self._handle)
+            _on(self._dev, lib().bca_decode_graph_destroy, self._handle)
             self._handle = _P()
 
     def __del__(self):
@@ -554,12 +562,10 @@ class DecodeLoop(DecodeGraph):
         self._keep = (q, k, v, kv_len_dev, steps_dev, workspace)
         self._dev = dev
         self._handle = _P()
-        st = lib().bca_decode_loop_create(_ptr(q), _ptr(k), _ptr(v), _ptr(self.out),
-                                          _ptr(self.lse), _ptr(kv_len_dev), _ptr(steps_dev),
-                                          q_len, kv_cap, hq,
-                                          hkv, d, scale, _dtype_code(q), int(num_splits),
-                                          _ptr(workspace), ws_bytes, int(steps),
-                                          ctypes.byref(self._handle))
+        st = _on(dev, lib().bca_decode_loop_create,
+                 _ptr(q), _ptr(k), _ptr(v), _ptr(self.out), _ptr(self.lse), _ptr(kv_len_dev),
+                 _ptr(steps_dev), q_len, kv_cap, hq, hkv, d, scale, _dtype_code(q), int(num_splits),
+                 _ptr(workspace), ws_bytes, int(steps), ctypes.byref(self._handle))
         _check("bca_decode_loop_create", st)
         self.steps = int(steps)
 

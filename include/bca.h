@@ -45,6 +45,14 @@
  * BCA_VALIDATE is set (below).  A max_seqlen below a segment's length leaves
  * that segment's first query tiles unwritten.
  *
+ * Device: as with HIP itself, the calling thread's current device must be
+ * the device that holds the pointers and owns `stream` (the no-allocation
+ * decode finds its scratch array, and the graph entry points create their
+ * capture stream, on the current device).
+ *
+ * Errors and exceptions: no C++ exception leaves the library; a host
+ * allocation that fails returns BCA_ERR_HOST_MEMORY.
+ *
  * Errors: every host-detectable fault (NULL pointer, bad shape or size,
  * unsupported head_dim or dtype, scale not finite or not > 0, workspace too
  * small) is reported by the return value before anything is enqueued.  A
