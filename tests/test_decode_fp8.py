@@ -37,7 +37,8 @@ def test_fp8_decode_matches_oracle(P):
 
 
 @pytest.mark.parametrize("P,B,hq,hkv,d", [(0, 32, 32, 8, 128), (100 * 2, 16, 4, 4, 128),
-                                          (960, 32, 16, 2, 64), (250, 48, 6, 2, 128)])
+                                          (960, 32, 16, 2, 64), (250, 48, 6, 2, 128),
+                                          (300, 40, 16, 8, 128)])
 def test_fp8_decode_edge_shapes(P, B, hq, hkv, d):
     w, k8, v8, ks, vs, o, lse = run(P, block_size=B, hq=hq, hkv=hkv, d=d, seed=9)
     K = oracle.e4m3_to_float(k8.numpy()) * ks

@@ -34,6 +34,9 @@ def test_decode_step_matches_oracle(P):
 @pytest.mark.parametrize("P,B,hq,hkv,d", [
     (0, 32, 32, 8, 128), (68, 16, 4, 4, 128), (1000, 32, 16, 2, 64), (200, 48, 6, 2, 128),
     (64 * 40, 64, 32, 8, 128),
+    # two query heads per KV head: a workgroup takes two 32-token sub-tiles,
+    # the second here partly past the block's 40 tokens
+    (300, 40, 16, 8, 128), (777, 40, 8, 4, 64),
 ])
 def test_decode_edge_shapes(P, B, hq, hkv, d):
     w = W.decode_step(P, block_size=B, hq=hq, hkv=hkv, d=d, seed=5)
